@@ -1,0 +1,143 @@
+"""CPU oracle for one beam-search decode step (test infrastructure only).
+
+Only the test suite, the package smoke check and the benchmark's CPU-baseline
+leg may import this package; the product path never does. The arithmetic
+lives in ``rtopk_oracle.c`` (plain C, float64): full log-softmax of every
+alive beam, one full sort per batch element by (score desc, flat index asc),
+as the LightSeq inference article's hierarchical-decoding passage states the
+problem before its rewrite. This module only marshals numpy arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "rtopk_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+F32, F16, BF16 = 0, 1, 2
+
+
+def build(force: bool = False) -> str:
+    """Compile liboracle.so with the host C compiler (gcc)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + f".tmp{os.getpid()}"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-shared", "-fPIC", _SRC, "-o", tmp,
+                               "-lm", "-lpthread"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(_LIB)
+        vp, i32, i64, f64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        L.rtopk_oracle_step.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, i32]
+        L.rtopk_oracle_step.restype = i32
+        L.rtopk_oracle_lse.argtypes = [vp, i32, i64, i64, vp]
+        L.rtopk_oracle_lse.restype = None
+        L.rtopk_oracle_score_of.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32]
+        L.rtopk_oracle_score_of.restype = f64
+        L.rtopk_oracle_threshold.argtypes = [vp, i32, i64, i64, i32, i32, i64]
+        L.rtopk_oracle_threshold.restype = f64
+        L.rtopk_oracle_count_ge.argtypes = [vp, i32, i64, i64, f64]
+        L.rtopk_oracle_count_ge.restype = i64
+        L.rtopk_oracle_decode_f16.argtypes = [ctypes.c_uint16]
+        L.rtopk_oracle_decode_f16.restype = f64
+        L.rtopk_oracle_decode_bf16.argtypes = [ctypes.c_uint16]
+        L.rtopk_oracle_decode_bf16.restype = f64
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _logits(x, dtype):
+    want = {F32: np.float32, F16: np.float16, BF16: np.uint16}[dtype]
+    x = np.ascontiguousarray(x)
+    if x.dtype != want:
+        raise TypeError(f"logits dtype {x.dtype} does not match code {dtype}")
+    return x
+
+
+class Result:
+    """Oracle output for one step: [B, k] beam/token/score, fp64 scores, [B, beam] lse."""
+
+    def __init__(self, beam_ids, token_ids, scores, scores64, lse):
+        self.beam_ids, self.token_ids, self.scores = beam_ids, token_ids, scores
+        self.scores64, self.lse = scores64, lse
+
+
+def step(logits, dtype, alive, finished, k, eos_id=2, nthreads=1) -> Result:
+    """Run the oracle on host arrays logits [B, beam, V], alive [B, beam], finished [B, beam] or None."""
+    L = _load()
+    x = _logits(logits, dtype)
+    B, beam, V = x.shape
+    alive = np.ascontiguousarray(alive, dtype=np.float32).reshape(B, beam)
+    fin = None if finished is None else np.ascontiguousarray(finished, dtype=np.uint8).reshape(B, beam)
+    ob = np.empty((B, k), np.int32)
+    ot = np.empty((B, k), np.int32)
+    os_ = np.empty((B, k), np.float32)
+    o64 = np.empty((B, k), np.float64)
+    lse = np.empty((B, beam), np.float64)
+    rc = L.rtopk_oracle_step(_ptr(x), dtype, _ptr(alive), _ptr(fin), B, beam, V, k, eos_id,
+                             _ptr(ob), _ptr(ot), _ptr(os_), _ptr(o64), _ptr(lse), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"rtopk_oracle_step failed with status {rc}")
+    return Result(ob, ot, os_, o64, lse)
+
+
+def step_of(s, nthreads=1) -> Result:
+    """Oracle on a ``synth.Step``."""
+    return step(s.logits, s.dtype, s.alive, s.finished, s.k, s.eos_id, nthreads)
+
+
+def lse(logits, dtype) -> np.ndarray:
+    """float64 log-sum-exp of every row of logits [..., V]."""
+    x = _logits(logits, dtype)
+    V = x.shape[-1]
+    nrows = x.size // V
+    out = np.empty(nrows, np.float64)
+    _load().rtopk_oracle_lse(_ptr(x), dtype, nrows, V, _ptr(out))
+    return out.reshape(x.shape[:-1])
+
+
+def score_of(logits, dtype, alive, finished, lse_, eos_id, b, j, t) -> float:
+    """The oracle's float64 score of pair (b, j, t); -inf for non-candidates and padding."""
+    x = _logits(logits, dtype)
+    B, beam, V = x.shape
+    alive = np.ascontiguousarray(alive, dtype=np.float32)
+    fin = None if finished is None else np.ascontiguousarray(finished, dtype=np.uint8)
+    lse_ = np.ascontiguousarray(lse_, dtype=np.float64)
+    return _load().rtopk_oracle_score_of(_ptr(x), dtype, _ptr(alive), _ptr(fin), _ptr(lse_),
+                                         B, beam, V, eos_id, int(b), int(j), int(t))
+
+
+def threshold(x, dtype, ngroups, k, offset=0, base=0, n=None) -> float:
+    """R-top-k of x[base:base+n] with element i in group (i + offset) mod ngroups."""
+    x = _logits(x, dtype)
+    n = x.size - base if n is None else n
+    return _load().rtopk_oracle_threshold(_ptr(x), dtype, base, n, ngroups, k, offset)
+
+
+def count_ge(x, dtype, T, base=0, n=None) -> int:
+    x = _logits(x, dtype)
+    n = x.size - base if n is None else n
+    return int(_load().rtopk_oracle_count_ge(_ptr(x), dtype, base, n, float(T)))
+
+
+def decode_f16(code: int) -> float:
+    return _load().rtopk_oracle_decode_f16(int(code))
+
+
+def decode_bf16(code: int) -> float:
+    return _load().rtopk_oracle_decode_bf16(int(code))
