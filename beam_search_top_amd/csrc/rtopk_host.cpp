@@ -1,0 +1,376 @@
+// Host side of the C ABI declared in include/rtopk.h: argument validation,
+// the decomposition of a call into workgroups, the workspace cache and the
+// launch. All argument checks run before any HIP call, so a rejected call
+// touches neither the GPU nor its outputs.
+//
+// The per-stream workspace follows the memory-reuse idea of the LightSeq
+// inference article (its memory-reuse passage): buffers are sized once and
+// reused on every request instead of being allocated per step.
+#include "rtopk.h"
+#include "rtopk_internal.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <atomic>
+#include <climits>
+#include <cstdarg>
+#include <cstdio>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int status, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return status;
+}
+
+std::atomic<int> g_override_nv{0};
+std::atomic<int> g_override_limit{0};
+
+const int kVecsPerThread[] = {1, 2, 3, 4, 6, 8, 10, 12, 16};
+// Most 16-byte vectors a thread holds without exceeding ~160 VGPRs (no
+// spills, >= 3 waves per SIMD): fp16 keeps its max on packed pairs and
+// needs fewer registers per vector than fp32 and bf16.
+int max_vecs_per_thread(int dtype) { return dtype == RTOPK_F16 ? 16 : 12; }
+// Workgroups wanted per launch before pieces are made smaller: 4 per CU on 256 CUs.
+constexpr long long kTargetGrid = 1024;
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
+
+int pow2_ceil(int x)
+{
+    int p = 1;
+    while (p < x)
+        p <<= 1;
+    return p;
+}
+
+// Validates the scalar arguments and computes the decomposition.
+int make_plan(const void *logits, int B, int beam, int V, int k, int dtype, rtopk::Plan *p)
+{
+    if (dtype != RTOPK_F32 && dtype != RTOPK_F16 && dtype != RTOPK_BF16)
+        return fail(RTOPK_EINVAL, "unknown dtype %d", dtype);
+    if (B < 1 || beam < 1 || V < 1 || k < 1)
+        return fail(RTOPK_EINVAL, "sizes must be >= 1 (B=%d beam=%d V=%d k=%d)", B, beam, V, k);
+    if ((long long)beam * V > INT_MAX)
+        return fail(RTOPK_EINVAL, "beam*V = %lld exceeds 2^31-1", (long long)beam * V);
+    if ((long long)k > (long long)beam * V)
+        return fail(RTOPK_EINVAL, "k=%d exceeds beam*V=%lld", k, (long long)beam * V);
+    if (k > RTOPK_MAX_K)
+        return fail(RTOPK_ENOTSUP, "k=%d exceeds the implementation limit %d", k, RTOPK_MAX_K);
+    if (beam > RTOPK_MAX_BEAM)
+        return fail(RTOPK_ENOTSUP, "beam=%d exceeds the implementation limit %d", beam, RTOPK_MAX_BEAM);
+
+    p->elem_bytes = dtype == RTOPK_F32 ? 4 : 2;
+    p->epv = 16 / p->elem_bytes;
+    const uintptr_t mis = logits ? (uintptr_t)logits % 16 : 0;
+    if (mis % p->elem_bytes)
+        return fail(RTOPK_EINVAL, "logits pointer is not aligned to its element size");
+    p->align_elems = (int)(mis / p->elem_bytes);
+    const bool aligned_rows = p->align_elems == 0 && V % p->epv == 0;
+    // 16-byte vectors one row touches at most
+    const long long span = aligned_rows ? V / p->epv : ceil_div(V, p->epv) + 1;
+    const long long rows = (long long)B * beam;
+
+    int nv = g_override_nv.load();
+    long long C;
+    if (nv > 0) {
+        C = ceil_div(span, (long long)rtopk::kThreads * nv);
+    } else {
+        const int nvmax = max_vecs_per_thread(dtype);
+        const long long c0 = ceil_div(span, (long long)rtopk::kThreads * nvmax);
+        C = c0;
+        if (rows * c0 < kTargetGrid) {
+            long long want = ceil_div(kTargetGrid, rows);
+            long long cmax = ceil_div(span, rtopk::kThreads); // one vector per thread
+            C = want < cmax ? want : cmax;
+            if (C < c0)
+                C = c0;
+        }
+        const long long need = ceil_div(span, (long long)rtopk::kThreads * C);
+        nv = nvmax;
+        for (int v : kVecsPerThread)
+            if (v >= need && v <= nvmax) {
+                nv = v;
+                break;
+            }
+        C = ceil_div(span, (long long)rtopk::kThreads * nv);
+    }
+    p->vecs_per_thread = nv;
+    p->chunks = (int)C;
+    // pieces hold exactly threads*nv vectors (so the kernel's unmasked path
+    // covers them), except a row's last piece, which holds the remainder
+    p->vecs_per_chunk = rtopk::kThreads * nv;
+    p->ngroups = pow2_ceil(k);
+    int lim = g_override_limit.load();
+    p->chunk_limit = lim > 0 ? lim : rtopk::kMaxChunkLimit;
+    if (p->chunk_limit < k)
+        p->chunk_limit = k; // a piece always may emit its own top-k
+    p->grid = rows * C;
+    if (p->grid > INT_MAX)
+        return fail(RTOPK_ENOTSUP, "grid of %lld workgroups is too large", p->grid);
+    const long long qcap = (long long)beam * C * p->chunk_limit;
+    if (qcap > INT_MAX)
+        return fail(RTOPK_ENOTSUP, "candidate queue of %lld entries is too large", qcap);
+    p->queue_cap = (int)qcap;
+
+    size_t off = 0;
+    p->ws_count_off = off;
+    off = align256(off + sizeof(uint32_t) * (size_t)B);
+    p->ws_ticket_off = off;
+    off = align256(off + sizeof(uint32_t) * (size_t)B);
+    p->ws_part_off = off;
+    off = align256(off + 16 * (size_t)rows * (size_t)C);
+    p->ws_queue_off = off;
+    off = align256(off + sizeof(uint64_t) * (size_t)B * (size_t)p->queue_cap);
+    p->ws_bytes = off;
+    return RTOPK_OK;
+}
+
+int check_pointers(const void *logits, const float *alive, const int32_t *ob, const int32_t *ot,
+                   const float *os)
+{
+    if (!logits)
+        return fail(RTOPK_EINVAL, "logits is NULL");
+    if (!alive)
+        return fail(RTOPK_EINVAL, "alive_scores is NULL");
+    if (!ob || !ot || !os)
+        return fail(RTOPK_EINVAL, "an output pointer is NULL");
+    return RTOPK_OK;
+}
+
+struct Debug {
+    float *T = nullptr;
+    uint32_t *hits = nullptr;
+    float *lse = nullptr;
+    uint32_t *count = nullptr;
+    uint64_t *queue = nullptr;
+};
+
+int enqueue(const rtopk::Plan &p, const void *logits, int dtype, const float *alive,
+            const uint8_t *finished, int B, int beam, int V, int k, int eos_id, int32_t *ob,
+            int32_t *ot, float *os, void *ws, const Debug &dbg, hipStream_t stream)
+{
+    rtopk::StepArgs a{};
+    a.logits_aligned = (const uint8_t *)logits - (size_t)p.align_elems * p.elem_bytes;
+    a.alive = alive;
+    a.finished = finished;
+    a.B = B;
+    a.beam = beam;
+    a.V = V;
+    a.k = k;
+    a.eos_id = eos_id;
+    a.align_elems = p.align_elems;
+    a.chunks = p.chunks;
+    a.vecs_per_chunk = p.vecs_per_chunk;
+    a.ngroups = p.ngroups;
+    a.chunk_limit = p.chunk_limit;
+    a.queue_cap = p.queue_cap;
+    uint8_t *w = (uint8_t *)ws;
+    a.count = (uint32_t *)(w + p.ws_count_off);
+    a.ticket = (uint32_t *)(w + p.ws_ticket_off);
+    a.part = (float4 *)(w + p.ws_part_off);
+    a.queue = (uint64_t *)(w + p.ws_queue_off);
+    a.out_beam = ob;
+    a.out_token = ot;
+    a.out_score = os;
+    a.dbg_T = dbg.T;
+    a.dbg_hits = dbg.hits;
+    a.dbg_lse = dbg.lse;
+    a.dbg_count = dbg.count;
+    a.dbg_queue = dbg.queue;
+    hipError_t e = rtopk::launch_step(a, dtype, p.vecs_per_thread, stream);
+    if (e != hipSuccess)
+        return fail(RTOPK_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return RTOPK_OK;
+}
+
+// ---------------------------------------------------------------- workspace cache
+struct WsEntry {
+    void *ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_ws_mu;
+std::map<std::pair<int, void *>, WsEntry> g_ws;
+
+int acquire_workspace(size_t need, hipStream_t stream, void **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(RTOPK_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    WsEntry &w = g_ws[{dev, (void *)stream}];
+    if (w.bytes < need) {
+        if (w.ptr) {
+            // earlier calls on this stream may still use the old buffer
+            e = hipStreamSynchronize(stream);
+            if (e != hipSuccess)
+                return fail(RTOPK_EHIP, "hipStreamSynchronize: %s", hipGetErrorString(e));
+            (void)hipFree(w.ptr);
+            w.ptr = nullptr;
+            w.bytes = 0;
+        }
+        size_t bytes = align256(need + need / 2);
+        void *p = nullptr;
+        e = hipMalloc(&p, bytes);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(RTOPK_ENOMEM, "hipMalloc(%zu) for the workspace: %s", bytes, hipGetErrorString(e));
+        }
+        e = rtopk::launch_zero(p, bytes, stream);
+        if (e != hipSuccess) {
+            (void)hipFree(p);
+            return fail(RTOPK_EHIP, "zero-filling the workspace: %s", hipGetErrorString(e));
+        }
+        w.ptr = p;
+        w.bytes = bytes;
+    }
+    *out = w.ptr;
+    return RTOPK_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+int rtopk_beam_step(const void *logits, int dtype, const float *alive_scores,
+                    const uint8_t *finished_mask, int B, int beam, int V, int k, int eos_id,
+                    int32_t *out_beam_ids, int32_t *out_token_ids, float *out_scores, void *stream)
+{
+    int st = check_pointers(logits, alive_scores, out_beam_ids, out_token_ids, out_scores);
+    if (st != RTOPK_OK)
+        return st;
+    rtopk::Plan p;
+    if ((st = make_plan(logits, B, beam, V, k, dtype, &p)) != RTOPK_OK)
+        return st;
+    if (eos_id < 0 || eos_id >= V)
+        return fail(RTOPK_EINVAL, "eos_id=%d outside [0, %d)", eos_id, V);
+    void *ws = nullptr;
+    if ((st = acquire_workspace(p.ws_bytes, (hipStream_t)stream, &ws)) != RTOPK_OK)
+        return st;
+    return enqueue(p, logits, dtype, alive_scores, finished_mask, B, beam, V, k, eos_id, out_beam_ids,
+                   out_token_ids, out_scores, ws, Debug{}, (hipStream_t)stream);
+}
+
+size_t rtopk_workspace_bytes(int B, int beam, int V, int k, int dtype)
+{
+    rtopk::Plan p;
+    if (make_plan(nullptr, B, beam, V, k, dtype, &p) != RTOPK_OK)
+        return 0;
+    // the largest misalignment can add one vector per row; size for it
+    rtopk::Plan q;
+    if (make_plan((const void *)(uintptr_t)(16 - (dtype == RTOPK_F32 ? 4 : 2)), B, beam, V, k, dtype, &q) !=
+        RTOPK_OK)
+        return p.ws_bytes;
+    return p.ws_bytes > q.ws_bytes ? p.ws_bytes : q.ws_bytes;
+}
+
+static int step_ws(const void *logits, int dtype, const float *alive_scores, const uint8_t *finished_mask,
+                   int B, int beam, int V, int k, int eos_id, int32_t *ob, int32_t *ot, float *os,
+                   void *workspace, size_t ws_bytes, const Debug &dbg, void *stream)
+{
+    int st = check_pointers(logits, alive_scores, ob, ot, os);
+    if (st != RTOPK_OK)
+        return st;
+    rtopk::Plan p;
+    if ((st = make_plan(logits, B, beam, V, k, dtype, &p)) != RTOPK_OK)
+        return st;
+    if (eos_id < 0 || eos_id >= V)
+        return fail(RTOPK_EINVAL, "eos_id=%d outside [0, %d)", eos_id, V);
+    if (!workspace)
+        return fail(RTOPK_EINVAL, "workspace is NULL");
+    if ((uintptr_t)workspace % 256)
+        return fail(RTOPK_EINVAL, "workspace is not 256-byte aligned");
+    if (ws_bytes < p.ws_bytes)
+        return fail(RTOPK_ENOMEM, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, p.ws_bytes);
+    return enqueue(p, logits, dtype, alive_scores, finished_mask, B, beam, V, k, eos_id, ob, ot, os,
+                   workspace, dbg, (hipStream_t)stream);
+}
+
+int rtopk_beam_step_ws(const void *logits, int dtype, const float *alive_scores,
+                       const uint8_t *finished_mask, int B, int beam, int V, int k, int eos_id,
+                       int32_t *out_beam_ids, int32_t *out_token_ids, float *out_scores, void *workspace,
+                       size_t ws_bytes, void *stream)
+{
+    return step_ws(logits, dtype, alive_scores, finished_mask, B, beam, V, k, eos_id, out_beam_ids,
+                   out_token_ids, out_scores, workspace, ws_bytes, Debug{}, stream);
+}
+
+int rtopk_debug_step(const void *logits, int dtype, const float *alive_scores,
+                     const uint8_t *finished_mask, int B, int beam, int V, int k, int eos_id,
+                     int32_t *out_beam_ids, int32_t *out_token_ids, float *out_scores, void *workspace,
+                     size_t ws_bytes, float *dbg_T, uint32_t *dbg_hits, float *dbg_lse,
+                     uint32_t *dbg_count, uint64_t *dbg_queue, void *stream)
+{
+    Debug d;
+    d.T = dbg_T;
+    d.hits = dbg_hits;
+    d.lse = dbg_lse;
+    d.count = dbg_count;
+    d.queue = dbg_queue;
+    return step_ws(logits, dtype, alive_scores, finished_mask, B, beam, V, k, eos_id, out_beam_ids,
+                   out_token_ids, out_scores, workspace, ws_bytes, d, stream);
+}
+
+int rtopk_plan(const void *logits, int B, int beam, int V, int k, int dtype, rtopk_plan_t *out)
+{
+    if (!out)
+        return fail(RTOPK_EINVAL, "out is NULL");
+    rtopk::Plan p;
+    int st = make_plan(logits, B, beam, V, k, dtype, &p);
+    if (st != RTOPK_OK)
+        return st;
+    out->chunks = p.chunks;
+    out->threads = rtopk::kThreads;
+    out->vecs_per_thread = p.vecs_per_thread;
+    out->vecs_per_chunk = p.vecs_per_chunk;
+    out->elems_per_vec = p.epv;
+    out->ngroups = p.ngroups;
+    out->chunk_limit = p.chunk_limit;
+    out->queue_cap = p.queue_cap;
+    out->align_elems = p.align_elems;
+    out->grid = (int)p.grid;
+    return RTOPK_OK;
+}
+
+int rtopk_set_override(int vecs_per_thread, int chunk_limit)
+{
+    if (vecs_per_thread != 0 && !rtopk::supported_vecs_per_thread(vecs_per_thread))
+        return fail(RTOPK_EINVAL, "vecs_per_thread=%d is not one of the built variants", vecs_per_thread);
+    if (chunk_limit < 0 || chunk_limit > rtopk::kMaxChunkLimit)
+        return fail(RTOPK_EINVAL, "chunk_limit=%d outside [0, %d]", chunk_limit, rtopk::kMaxChunkLimit);
+    g_override_nv.store(vecs_per_thread);
+    g_override_limit.store(chunk_limit);
+    return RTOPK_OK;
+}
+
+const char *rtopk_last_error(void) { return g_err.c_str(); }
+
+void rtopk_release(void)
+{
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    for (auto &kv : g_ws) {
+        if (kv.second.ptr) {
+            (void)hipSetDevice(kv.first.first);
+            (void)hipDeviceSynchronize();
+            (void)hipFree(kv.second.ptr);
+        }
+    }
+    g_ws.clear();
+}
+
+} // extern "C"

@@ -1,0 +1,221 @@
+"""Thin ctypes binding of librtopk.so (declared in include/rtopk.h).
+
+The ``rtopk_*`` functions take integer device addresses and sizes, exactly like
+the C ABI, and return its status codes. ``beam_step`` marshals torch tensors
+(torch is used only for device memory and the current stream) and raises on a
+non-OK status. Every step of the selection runs in the HIP kernels; there is no
+fallback: without a built librtopk.so the import of this module's functions
+fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "librtopk.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "rtopk.h")
+
+RTOPK_F32, RTOPK_F16, RTOPK_BF16 = 0, 1, 2
+RTOPK_OK, RTOPK_EINVAL, RTOPK_ENOTSUP, RTOPK_ENOMEM, RTOPK_EHIP = 0, -1, -2, -3, -4
+RTOPK_MAX_K, RTOPK_MAX_BEAM = 64, 512
+STATUS_NAMES = {0: "RTOPK_OK", -1: "RTOPK_EINVAL", -2: "RTOPK_ENOTSUP", -3: "RTOPK_ENOMEM", -4: "RTOPK_EHIP"}
+
+
+class RtopkError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class rtopk_plan_t(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in (
+        "chunks", "threads", "vecs_per_thread", "vecs_per_chunk", "elems_per_vec", "ngroups",
+        "chunk_limit", "queue_cap", "align_elems", "grid")]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+_lib = None
+
+
+def load():
+    """Load librtopk.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m beam_search_top_amd._build` "
+                          "(or __graft_entry__.build()); there is no fallback path")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    step_args = [vp, i32, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp]
+    L.rtopk_beam_step.argtypes = step_args + [vp]
+    L.rtopk_beam_step.restype = i32
+    L.rtopk_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    L.rtopk_workspace_bytes.restype = sz
+    L.rtopk_beam_step_ws.argtypes = step_args + [vp, sz, vp]
+    L.rtopk_beam_step_ws.restype = i32
+    L.rtopk_debug_step.argtypes = step_args + [vp, sz, vp, vp, vp, vp, vp, vp]
+    L.rtopk_debug_step.restype = i32
+    L.rtopk_plan.argtypes = [vp, i32, i32, i32, i32, i32, ctypes.POINTER(rtopk_plan_t)]
+    L.rtopk_plan.restype = i32
+    L.rtopk_set_override.argtypes = [i32, i32]
+    L.rtopk_set_override.restype = i32
+    L.rtopk_last_error.argtypes = []
+    L.rtopk_last_error.restype = ctypes.c_char_p
+    L.rtopk_release.argtypes = []
+    L.rtopk_release.restype = None
+    _lib = L
+    return L
+
+
+def declared_functions(header=HEADER):
+    """Names of the functions include/rtopk.h declares."""
+    text = open(header).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rtopk_[a-z0-9_]+)\s*\(", text)))
+
+
+# ------------------------------------------------------------------ C-ABI mirror
+def rtopk_beam_step(logits, dtype, alive_scores, finished_mask, B, beam, V, k, eos_id,
+                    out_beam_ids, out_token_ids, out_scores, stream):
+    return load().rtopk_beam_step(logits, dtype, alive_scores, finished_mask, B, beam, V, k, eos_id,
+                                  out_beam_ids, out_token_ids, out_scores, stream)
+
+
+def rtopk_workspace_bytes(B, beam, V, k, dtype):
+    return load().rtopk_workspace_bytes(B, beam, V, k, dtype)
+
+
+def rtopk_beam_step_ws(logits, dtype, alive_scores, finished_mask, B, beam, V, k, eos_id,
+                       out_beam_ids, out_token_ids, out_scores, workspace, ws_bytes, stream):
+    return load().rtopk_beam_step_ws(logits, dtype, alive_scores, finished_mask, B, beam, V, k, eos_id,
+                                     out_beam_ids, out_token_ids, out_scores, workspace, ws_bytes, stream)
+
+
+def rtopk_debug_step(logits, dtype, alive_scores, finished_mask, B, beam, V, k, eos_id,
+                     out_beam_ids, out_token_ids, out_scores, workspace, ws_bytes,
+                     dbg_T, dbg_hits, dbg_lse, dbg_count, dbg_queue, stream):
+    return load().rtopk_debug_step(logits, dtype, alive_scores, finished_mask, B, beam, V, k, eos_id,
+                                   out_beam_ids, out_token_ids, out_scores, workspace, ws_bytes,
+                                   dbg_T, dbg_hits, dbg_lse, dbg_count, dbg_queue, stream)
+
+
+def rtopk_plan(logits, B, beam, V, k, dtype):
+    """Returns (status, rtopk_plan_t)."""
+    p = rtopk_plan_t()
+    st = load().rtopk_plan(logits, B, beam, V, k, dtype, ctypes.byref(p))
+    return st, p
+
+
+def rtopk_set_override(vecs_per_thread, chunk_limit):
+    return load().rtopk_set_override(vecs_per_thread, chunk_limit)
+
+
+def rtopk_last_error():
+    return load().rtopk_last_error().decode()
+
+
+def rtopk_release():
+    load().rtopk_release()
+
+
+# ------------------------------------------------------------------ torch marshalling
+def _check(status):
+    if status != RTOPK_OK:
+        raise RtopkError(status, rtopk_last_error())
+
+
+def dtype_code(t):
+    import torch
+    codes = {torch.float32: RTOPK_F32, torch.float16: RTOPK_F16, torch.bfloat16: RTOPK_BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"logits dtype {t.dtype} is not float32/float16/bfloat16")
+    return codes[t.dtype]
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _prepare(logits, alive, finished, k):
+    import torch
+    if logits.dim() != 3:
+        raise ValueError("logits must be [B, beam, V]")
+    if not logits.is_cuda:
+        raise ValueError("logits must be a device tensor")
+    B, beam, V = logits.shape
+    if not logits.is_contiguous():
+        raise ValueError("logits must be contiguous")
+    if alive.shape != (B, beam) or alive.dtype != torch.float32 or not alive.is_contiguous():
+        raise ValueError("alive must be a contiguous float32 [B, beam] tensor")
+    if finished is not None:
+        if finished.shape != (B, beam) or finished.dtype not in (torch.uint8, torch.bool):
+            raise ValueError("finished must be a [B, beam] uint8/bool tensor")
+        finished = finished.contiguous()
+        if finished.dtype == torch.bool:
+            finished = finished.view(torch.uint8)
+    dev = logits.device
+    outs = (torch.empty((B, k), dtype=torch.int32, device=dev),
+            torch.empty((B, k), dtype=torch.int32, device=dev),
+            torch.empty((B, k), dtype=torch.float32, device=dev))
+    return B, beam, V, finished, outs
+
+
+def beam_step(logits, alive, finished=None, k=None, eos_id=2, workspace=None, out=None):
+    """One selection step on torch device tensors, on the current stream.
+
+    logits [B, beam, V] float32/float16/bfloat16, alive [B, beam] float32,
+    finished [B, beam] bool/uint8 or None. Returns (beam_ids, token_ids,
+    scores), each [B, k]. ``workspace`` (a zero-filled uint8 device tensor of
+    rtopk_workspace_bytes(...) bytes) selects rtopk_beam_step_ws; ``out`` may
+    supply the three output tensors.
+    """
+    import torch
+    if k is None:
+        k = logits.shape[1]
+    B, beam, V, finished, outs = _prepare(logits, alive, finished, k)
+    if out is not None:
+        outs = out
+    stream = torch.cuda.current_stream(logits.device).cuda_stream
+    args = (_ptr(logits), dtype_code(logits), _ptr(alive), _ptr(finished), B, beam, V, k, eos_id,
+            _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]))
+    if workspace is None:
+        _check(rtopk_beam_step(*args, stream))
+    else:
+        _check(rtopk_beam_step_ws(*args, _ptr(workspace), workspace.numel() * workspace.element_size(), stream))
+    return outs
+
+
+def debug_step(logits, alive, finished=None, k=None, eos_id=2):
+    """beam_step plus the kernel's intermediate values (for tests).
+
+    Returns a dict with the outputs and the plan, the per-piece thresholds
+    T [B*beam*chunks], hit counts, merged lse [B*beam], per-batch queue
+    counts and the raw queue [B, queue_cap] (uint64 entries).
+    """
+    import torch
+    if k is None:
+        k = logits.shape[1]
+    B, beam, V, finished, outs = _prepare(logits, alive, finished, k)
+    code = dtype_code(logits)
+    st, plan = rtopk_plan(_ptr(logits), B, beam, V, k, code)
+    _check(st)
+    dev = logits.device
+    nbytes = rtopk_workspace_bytes(B, beam, V, k, code)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+    npieces = B * beam * plan.chunks
+    dT = torch.full((npieces,), float("nan"), dtype=torch.float32, device=dev)
+    dh = torch.zeros(npieces, dtype=torch.int32, device=dev)
+    dl = torch.zeros(B * beam, dtype=torch.float32, device=dev)
+    dc = torch.zeros(B, dtype=torch.int32, device=dev)
+    dq = torch.zeros((B, plan.queue_cap), dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    _check(rtopk_debug_step(_ptr(logits), code, _ptr(alive), _ptr(finished), B, beam, V, k, eos_id,
+                            _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]), _ptr(ws), nbytes,
+                            _ptr(dT), _ptr(dh), _ptr(dl), _ptr(dc), _ptr(dq), stream))
+    return dict(beam_ids=outs[0], token_ids=outs[1], scores=outs[2], plan=plan.as_dict(), T=dT, hits=dh,
+                lse=dl, count=dc, queue=dq, workspace=ws)

@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Throughput of the hierarchical beam-search selection step on one MI355X.
+
+One step = one rtopk_beam_step call over a whole [B, beam, V] logit tensor
+(pass 1, pass 2, per-batch sort: the entire path, one kernel launch). The
+default workload is the B=128, beam=4, k=4, V=40000 fp16 configuration with
+26 of 512 beams finished. Inputs are seeded synthetic logits, resident in HBM
+before the timed region; the step rotates through a pool of distinct logit
+buffers larger than the 256 MB Infinity Cache so every step reads cold HBM.
+
+Prints one JSON line: beam-steps/s (whole job), logit GB/s against the 8 TB/s
+HBM peak (roofline of the one kernel), and the CPU oracle's throughput on the
+host cores as a baseline.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config b128]
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_rtopk_step_b128.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "beam_search_top_amd", "csrc", f)
+                  for f in ("rtopk_kernels.hip", "rtopk_host.cpp", "rtopk_internal.h")]
+
+
+def kernel_sha():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(s):
+    """Bytes the method must move once: every alive logit row, the running
+    scores and finished mask, and the [B, k] outputs (ids and scores)."""
+    esz = {0: 4, 1: 2, 2: 2}[s.dtype]
+    alive_rows = s.B * s.beam - s.n_finished
+    return alive_rows * s.V * esz + 4 * s.B * s.beam + s.B * s.beam + 12 * s.B * s.k
+
+
+def read_traffic(config):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    if config != "b128" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                vals[key.strip()] = val.strip()
+    if vals.get("kernel_sha") != kernel_sha():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(s, seconds):
+    import oracle
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    oracle.step_of(s, nthreads=threads)  # warm (page-in)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.step_of(s, nthreads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 1000:
+            break
+    return {"value": reps / el, "unit": "beam-steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} full {s.name} steps (B={s.B} beam={s.beam} V={s.V}) in {el:.1f} s, "
+                      f"float64 log-softmax + full sort per batch element, {threads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--config", default="b128")
+    ap.add_argument("--launch", default="graph", choices=["graph", "eager"],
+                    help="replay the K launches from a captured HIP graph, or launch each from Python")
+    ap.add_argument("--pool-mib", type=int, default=1024, help="distinct logit buffers rotated through")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 256 MiB device copy (reference kernel for HBM counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the selection step of a batch "
+              "element needs no other GPU, and this build measures the one-GPU kernel.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from beam_search_top_amd import rtopk, synth
+
+    if not os.path.exists(rtopk.LIB_PATH):
+        from beam_search_top_amd import _build
+        _build.build()
+    rtopk.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    s = synth.make_step(args.config)
+    if s.dtype == synth.BF16:
+        x0 = torch.from_numpy(s.logits.view(np.int16)).view(torch.bfloat16).to(dev)
+    else:
+        x0 = torch.from_numpy(s.logits).to(dev)
+    alive = torch.from_numpy(s.alive).to(dev)
+    fin = torch.from_numpy(s.finished).to(dev)
+    nbuf = max(1, math.ceil(args.pool_mib * 2**20 / s.logit_bytes))
+    pool = [x0] + [torch.roll(x0, shifts=7919 * i, dims=2).contiguous() for i in range(1, nbuf)]
+    ob = torch.empty((s.B, s.k), dtype=torch.int32, device=dev)
+    ot = torch.empty((s.B, s.k), dtype=torch.int32, device=dev)
+    osc = torch.empty((s.B, s.k), dtype=torch.float32, device=dev)
+    nws = rtopk.rtopk_workspace_bytes(s.B, s.beam, s.V, s.k, s.dtype)
+    ws = torch.zeros(nws, dtype=torch.uint8, device=dev)
+    st, plan = rtopk.rtopk_plan(x0.data_ptr(), s.B, s.beam, s.V, s.k, s.dtype)
+    assert st == 0, rtopk.rtopk_last_error()
+    L = rtopk.load()
+    fixed = (s.dtype, alive.data_ptr(), fin.data_ptr(), s.B, s.beam, s.V, s.k, s.eos_id,
+             ob.data_ptr(), ot.data_ptr(), osc.data_ptr())
+    ptrs = [p.data_ptr() for p in pool]
+    wsp = ws.data_ptr()
+
+    def launch(i, stream):
+        rc = L.rtopk_beam_step_ws(ptrs[i % nbuf], *fixed, wsp, nws, stream)
+        if rc != 0:
+            raise RuntimeError(rtopk.rtopk_last_error())
+
+    torch.cuda.synchronize()
+    cur = torch.cuda.current_stream()
+    # warmup (eager)
+    for i in range(args.warmup):
+        launch(i, cur.cuda_stream)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    graph, glen = None, 0
+    if args.launch == "graph":
+        glen = min(K, 100)
+        graph = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream()
+        cs.wait_stream(cur)
+        with torch.cuda.graph(graph, stream=cs):
+            for i in range(glen):
+                launch(i, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+
+    def timed(mode):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(cur)
+        if mode == "graph":
+            for _ in range(K // glen):
+                graph.replay()
+            for i in range(K % glen):
+                launch(i, cur.cuda_stream)
+        else:
+            for i in range(K):
+                launch(i, cur.cuda_stream)
+        end.record(cur)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end)
+
+    ms_total = timed(args.launch)
+    ms_step = ms_total / K
+    other = {}
+    if args.launch == "graph":
+        other["eager_ms_per_step"] = round(timed("eager") / K, 6)
+
+    # the last step's outputs come from buffer (K-1) % nbuf; re-run buffer 0 for a sanity check
+    launch(0, cur.cuda_stream)
+    torch.cuda.synchronize()
+    assert (ob >= -1).all() and (ob < s.beam).all(), "beam ids out of range"
+
+    if args.copy_calibration:
+        n = 256 * 2**20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    alg = algorithmic_bytes(s)
+    achieved = alg / (ms_step * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(s, args.cpu_seconds)
+    dtype_name = {0: "f32", 1: "f16", 2: "bf16"}[s.dtype]
+    line = {
+        "metric": "beam-steps/sec and logit GB/s (% HBM peak) at BxbeamxV, 1xMI355X",
+        "value": 1e3 / ms_step,
+        "unit": "beam-steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype_name,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{s.name}: B={s.B} beam={s.beam} k={s.k} V={s.V} {dtype_name} logits, "
+                        f"{s.n_finished}/{s.B * s.beam} beams finished, seed {s.seed}",
+            "B": s.B, "beam": s.beam, "k": s.k, "V": s.V, "launch": args.launch,
+            "logit_pool_buffers": nbuf, "chunks": plan.chunks, "vecs_per_thread": plan.vecs_per_thread,
+            "grid": plan.grid,
+        },
+        "sequences_per_s": s.B * 1e3 / ms_step,
+        "logit_GBps": achieved,
+        "hbm_frac": achieved / HBM_PEAK_GBPS,
+        "algorithmic_bytes_per_step": alg,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": read_traffic(args.config)},
+        "cpu_baseline": cpu,
+        "kernel_sha": kernel_sha(),
+    }
+    line.update(other)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

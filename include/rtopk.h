@@ -1,0 +1,172 @@
+/*
+ * rtopk.h -- C ABI of the MI355X (gfx950) hierarchical beam-search selection step.
+ *
+ * One decode step of beam search, as stated by the LightSeq inference
+ * article (hierarchical-decoding passage): from a [batch_size, beam_size,
+ * vocab_size] logit matrix pick, for every batch element, the k best
+ * (beam, token) continuations, where the score of a continuation is the
+ * beam's running score plus the token's log-softmax:
+ *
+ *     score(b, j, t) = alive_scores[b][j] + logits[b][j][t] - lse(b, j),
+ *     lse(b, j)      = log(sum_t exp(logits[b][j][t])).
+ *
+ * The article's rewrite -- a first pass that splits each beam's logits into k
+ * groups, takes the minimum of the k group maxima as a lower bound (the
+ * "R-top-k") of the k-th largest logit and computes log_sum_exp in the same
+ * traversal, a second pass that keeps only logits >= R-top-k in a per-batch
+ * candidate queue, and one small sort of that queue -- gives exactly this
+ * result without a softmax or a sort over all beam*vocab elements.
+ *
+ * Conventions for every entry point below:
+ *  - Pointers marked "device" are HIP device memory owned by the caller; the
+ *    library never frees or retains them. They must stay valid until the work
+ *    enqueued on `stream` has completed.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Calls
+ *    are asynchronous: they validate, enqueue and return. Results are valid
+ *    once the stream reaches them.
+ *  - Validation is synchronous and happens before anything is enqueued; on a
+ *    non-OK status nothing was launched and no output was written.
+ *    rtopk_last_error() then describes the problem.
+ *  - Layouts are C-contiguous row-major. Logits may have any base alignment
+ *    that is a multiple of the element size.
+ *  - Output order per batch element: score descending, equal scores by the
+ *    lower flat index j*V + t. When fewer than k candidates exist (possible
+ *    only when finished beams leave fewer than k), the tail is padded with
+ *    beam = token = -1 and score = -inf.
+ *  - Finished beams (finished_mask != 0) are not read: each offers the single
+ *    continuation (j, eos_id) at its unchanged running score.
+ *  - Scores are computed in float32: alive + (logit - lse), lse accumulated in
+ *    float32 in a fixed order, so results are bit-reproducible across calls.
+ *  - NaN or +inf logits, and alive beams whose logits are all -inf, are
+ *    outside the contract (unspecified output, no error). Individual -inf
+ *    logits are fine.
+ */
+#ifndef RTOPK_H
+#define RTOPK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Logit storage types. */
+typedef enum { RTOPK_F32 = 0, RTOPK_F16 = 1, RTOPK_BF16 = 2 } rtopk_dtype;
+
+/* Status codes returned by the entry points. */
+typedef enum {
+    RTOPK_OK = 0,
+    RTOPK_EINVAL = -1,  /* bad argument: NULL pointer, size < 1, k > beam*V, eos outside [0,V), ... */
+    RTOPK_ENOTSUP = -2, /* valid but beyond the implementation limits: k > 64, beam > 512 */
+    RTOPK_ENOMEM = -3,  /* device allocation failed, or a caller workspace is too small */
+    RTOPK_EHIP = -4     /* a HIP runtime call or kernel launch failed */
+} rtopk_status;
+
+/* Implementation limits. */
+#define RTOPK_MAX_K 64
+#define RTOPK_MAX_BEAM 512
+
+/*
+ * How one call is decomposed (reported by rtopk_plan; the kernel uses it).
+ * Each beam's row is split into `chunks` contiguous pieces of at most
+ * `vecs_per_chunk` 16-byte vectors, one workgroup of `threads` threads per
+ * piece, each thread holding `vecs_per_thread` vectors in registers. Within a
+ * piece, element e (counted from the 16-byte-aligned address at or below the
+ * logits base pointer) belongs to group e mod `ngroups`; ngroups is k rounded
+ * up to a power of two and the piece's threshold is the k-th largest group
+ * maximum (the minimum when ngroups == k). A piece with more than
+ * `chunk_limit` logits at or above its threshold emits only its own exact
+ * top-k; `queue_cap` is the candidate-queue length per batch element.
+ */
+typedef struct {
+    int chunks;          /* pieces per beam row (C) */
+    int threads;         /* threads per workgroup */
+    int vecs_per_thread; /* 16-byte vectors held per thread */
+    int vecs_per_chunk;  /* 16-byte vectors per piece */
+    int elems_per_vec;   /* 4 for float32, 8 for float16/bfloat16 */
+    int ngroups;         /* groups of the threshold pass */
+    int chunk_limit;     /* candidates a piece may emit before switching to its exact top-k */
+    int queue_cap;       /* candidate-queue entries per batch element */
+    int align_elems;     /* misalignment of the logits base, in elements */
+    int grid;            /* workgroups launched: B * beam * chunks */
+} rtopk_plan_t;
+
+/*
+ * One beam-search selection step.
+ *   logits         device [B][beam][V], element type `dtype`
+ *   alive_scores   device [B][beam] float32 running log-probability scores
+ *   finished_mask  device [B][beam] uint8, nonzero = finished; NULL = none finished
+ *   B, beam, V, k  batch size, beams per batch element, vocabulary size, outputs per
+ *                  batch element; 1 <= k <= min(64, beam*V), beam <= 512, beam*V < 2^31
+ *   eos_id         token offered by a finished beam, in [0, V)
+ *   out_beam_ids   device [B][k] int32, in [0, beam) or -1
+ *   out_token_ids  device [B][k] int32, in [0, V) or -1
+ *   out_scores     device [B][k] float32
+ * Uses a workspace owned by the library, cached per (device, stream): the first
+ * call for a given stream (or for a larger shape) allocates and zero-fills it,
+ * later calls allocate nothing. Calls on one stream are serialised by the
+ * stream; concurrent calls on different streams use different workspaces.
+ */
+int rtopk_beam_step(const void *logits, int dtype, const float *alive_scores,
+                    const uint8_t *finished_mask, int B, int beam, int V, int k, int eos_id,
+                    int32_t *out_beam_ids, int32_t *out_token_ids, float *out_scores,
+                    void *stream);
+
+/* Bytes of caller workspace rtopk_beam_step_ws needs for this shape (0 on bad arguments). */
+size_t rtopk_workspace_bytes(int B, int beam, int V, int k, int dtype);
+
+/*
+ * rtopk_beam_step with a caller-owned device workspace of ws_bytes >=
+ * rtopk_workspace_bytes(...) bytes, 256-byte aligned. It must be zero-filled
+ * before its first use; every completed call leaves it ready for the next, for
+ * any shape that fits. Calls sharing one workspace must be ordered (same
+ * stream). Allocates nothing. RTOPK_ENOMEM when ws_bytes is too small.
+ */
+int rtopk_beam_step_ws(const void *logits, int dtype, const float *alive_scores,
+                       const uint8_t *finished_mask, int B, int beam, int V, int k, int eos_id,
+                       int32_t *out_beam_ids, int32_t *out_token_ids, float *out_scores,
+                       void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * rtopk_beam_step_ws that also copies out intermediate values (for tests):
+ *   dbg_T       device [B*beam*chunks] float32: each piece's threshold (-inf if empty)
+ *   dbg_hits    device [B*beam*chunks] uint32: logits >= threshold in the piece
+ *   dbg_lse     device [B*beam] float32: merged log-sum-exp (NaN for finished beams)
+ *   dbg_count   device [B] uint32: candidate-queue entries of each batch element
+ *   dbg_queue   device [B*queue_cap] uint64: the queue, entry = (float32 bits of the
+ *               logit << 32) | (j*V + t); only the first dbg_count[b] are defined
+ * Any debug pointer may be NULL. Finished beams leave their dbg_T/dbg_hits unset.
+ */
+int rtopk_debug_step(const void *logits, int dtype, const float *alive_scores,
+                     const uint8_t *finished_mask, int B, int beam, int V, int k, int eos_id,
+                     int32_t *out_beam_ids, int32_t *out_token_ids, float *out_scores,
+                     void *workspace, size_t ws_bytes, float *dbg_T, uint32_t *dbg_hits,
+                     float *dbg_lse, uint32_t *dbg_count, uint64_t *dbg_queue, void *stream);
+
+/*
+ * The decomposition a call with these arguments would use. `logits` is only
+ * inspected for its alignment (may be NULL = 16-byte aligned). Host only.
+ */
+int rtopk_plan(const void *logits, int B, int beam, int V, int k, int dtype, rtopk_plan_t *out);
+
+/*
+ * Process-wide tuning overrides for experiments and tests (0 = automatic):
+ * vecs_per_thread forces the 16-byte vectors each thread holds (one of
+ * 1,2,3,4,6,8,10,12,16; others are rejected with RTOPK_EINVAL);
+ * chunk_limit forces the per-piece candidate limit (1..256), which makes the
+ * exact per-piece top-k path run whenever a piece has more candidates.
+ */
+int rtopk_set_override(int vecs_per_thread, int chunk_limit);
+
+/* Thread-local description of the last non-OK status ("" if none). */
+const char *rtopk_last_error(void);
+
+/* Frees every cached library-owned workspace (synchronises their streams). */
+void rtopk_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RTOPK_H */

@@ -1,0 +1,135 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/rtopk.h declares, validates arguments before touching HIP, and plans
+the decomposition consistently. No call here reaches a kernel launch."""
+import ctypes
+import math
+
+import pytest
+
+from beam_search_top_amd import rtopk
+from libutil import ensure_built
+
+FAKE = 0x7000_0000  # never dereferenced: every call below fails validation first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ensure_built()
+
+
+def test_exports_every_declared_function(lib):
+    names = rtopk.declared_functions()
+    assert set(names) >= {"rtopk_beam_step", "rtopk_beam_step_ws", "rtopk_workspace_bytes",
+                          "rtopk_debug_step", "rtopk_plan", "rtopk_set_override",
+                          "rtopk_last_error", "rtopk_release"}
+    for n in names:
+        assert hasattr(lib, n), n
+        assert callable(getattr(rtopk, n)), n  # the binding mirrors every name
+
+
+def _step(**kw):
+    a = dict(logits=FAKE, dtype=1, alive=FAKE, fin=None, B=2, beam=4, V=100, k=4, eos=2,
+             ob=FAKE, ot=FAKE, os=FAKE)
+    a.update(kw)
+    return rtopk.rtopk_beam_step(a["logits"], a["dtype"], a["alive"], a["fin"], a["B"], a["beam"], a["V"],
+                                 a["k"], a["eos"], a["ob"], a["ot"], a["os"], None)
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(logits=None), rtopk.RTOPK_EINVAL, "logits"),
+    (dict(alive=None), rtopk.RTOPK_EINVAL, "alive"),
+    (dict(ob=None), rtopk.RTOPK_EINVAL, "output"),
+    (dict(ot=None), rtopk.RTOPK_EINVAL, "output"),
+    (dict(os=None), rtopk.RTOPK_EINVAL, "output"),
+    (dict(dtype=3), rtopk.RTOPK_EINVAL, "dtype"),
+    (dict(dtype=-1), rtopk.RTOPK_EINVAL, "dtype"),
+    (dict(B=0), rtopk.RTOPK_EINVAL, "sizes"),
+    (dict(beam=0), rtopk.RTOPK_EINVAL, "sizes"),
+    (dict(V=0), rtopk.RTOPK_EINVAL, "sizes"),
+    (dict(k=0), rtopk.RTOPK_EINVAL, "sizes"),
+    (dict(k=-3), rtopk.RTOPK_EINVAL, "sizes"),
+    (dict(beam=2, V=3, k=7), rtopk.RTOPK_EINVAL, "exceeds beam*V"),
+    (dict(beam=4, V=2**30), rtopk.RTOPK_EINVAL, "2^31"),
+    (dict(eos=100), rtopk.RTOPK_EINVAL, "eos_id"),
+    (dict(eos=-1), rtopk.RTOPK_EINVAL, "eos_id"),
+    (dict(k=65, beam=8), rtopk.RTOPK_ENOTSUP, "limit"),
+    (dict(beam=513, k=4), rtopk.RTOPK_ENOTSUP, "limit"),
+    (dict(logits=FAKE + 1), rtopk.RTOPK_EINVAL, "aligned"),
+    (dict(logits=FAKE + 2, dtype=0), rtopk.RTOPK_EINVAL, "aligned"),
+])
+def test_validation_rejects_before_launch(lib, kw, status, msg):
+    assert _step(**kw) == status
+    assert msg in rtopk.rtopk_last_error()
+
+
+def test_ws_entry_validation(lib):
+    args = (FAKE, 1, FAKE, None, 2, 4, 100, 4, 2, FAKE, FAKE, FAKE)
+    need = rtopk.rtopk_workspace_bytes(2, 4, 100, 4, 1)
+    assert need > 0
+    assert rtopk.rtopk_beam_step_ws(*args, None, need, None) == rtopk.RTOPK_EINVAL
+    assert rtopk.rtopk_beam_step_ws(*args, FAKE + 8, need, None) == rtopk.RTOPK_EINVAL  # not 256-aligned
+    assert rtopk.rtopk_beam_step_ws(*args, FAKE, need - 1, None) == rtopk.RTOPK_ENOMEM
+    assert "smaller" in rtopk.rtopk_last_error()
+    dbg = (None,) * 5
+    assert rtopk.rtopk_debug_step(*args, FAKE, need - 256, *dbg, None) == rtopk.RTOPK_ENOMEM
+    assert rtopk.rtopk_workspace_bytes(0, 4, 100, 4, 1) == 0
+
+
+def test_last_error_is_thread_local(lib):
+    import threading
+    _step(B=0)
+    seen = {}
+
+    def other():
+        seen["msg"] = rtopk.rtopk_last_error()
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["msg"] == ""
+    assert "sizes" in rtopk.rtopk_last_error()
+
+
+@pytest.mark.parametrize("shape", [
+    (2, 2, 8, 2, 0), (8, 4, 32000, 4, 0), (32, 4, 40000, 4, 1), (128, 4, 40000, 4, 1),
+    (64, 8, 250000, 8, 2), (1, 1, 1, 1, 0), (3, 5, 1001, 3, 1), (2, 16, 5000, 64, 2), (7, 3, 37, 5, 0),
+])
+def test_plan_covers_rows(lib, shape):
+    B, beam, V, k, dt = shape
+    for mis in (0, 1, 3):
+        esz = 4 if dt == 0 else 2
+        base = None if mis == 0 else FAKE + mis * esz
+        st, p = rtopk.rtopk_plan(base, B, beam, V, k, dt)
+        assert st == 0, rtopk.rtopk_last_error()
+        epv = 16 // esz
+        assert p.elems_per_vec == epv and p.threads == 256
+        assert p.align_elems == (mis % epv)
+        span = (p.align_elems + V + epv - 1) // epv if (p.align_elems or V % epv) else V // epv
+        # every vector a row touches lies in one of its pieces
+        assert p.chunks * p.vecs_per_chunk >= span + (1 if (p.align_elems or V % epv) else 0) - 1
+        assert p.vecs_per_chunk == p.threads * p.vecs_per_thread
+        assert p.grid == B * beam * p.chunks
+        assert p.ngroups >= k and p.ngroups & (p.ngroups - 1) == 0 and p.ngroups < 2 * k
+        assert p.chunk_limit >= k
+        assert p.queue_cap == beam * p.chunks * p.chunk_limit
+        need = rtopk.rtopk_workspace_bytes(B, beam, V, k, dt)
+        assert need >= 8 * B * p.queue_cap + 16 * B * beam * p.chunks
+
+
+def test_overrides(lib):
+    try:
+        assert rtopk.rtopk_set_override(5, 0) == rtopk.RTOPK_EINVAL
+        assert rtopk.rtopk_set_override(0, 257) == rtopk.RTOPK_EINVAL
+        assert rtopk.rtopk_set_override(0, -1) == rtopk.RTOPK_EINVAL
+        assert rtopk.rtopk_set_override(4, 1) == 0
+        st, p = rtopk.rtopk_plan(None, 4, 4, 40000, 4, 1)
+        assert st == 0 and p.vecs_per_thread == 4 and p.chunk_limit == 4  # raised to k
+        assert p.chunks == math.ceil(5000 / (256 * 4))
+    finally:
+        rtopk.rtopk_set_override(0, 0)
+    st, p = rtopk.rtopk_plan(None, 4, 4, 40000, 4, 1)
+    assert p.chunk_limit == 256
+
+
+def test_release_without_workspaces_is_harmless(lib):
+    rtopk.rtopk_release()

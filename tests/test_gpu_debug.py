@@ -1,0 +1,172 @@
+"""Intermediate values of the HIP path checked against the oracle's own
+pass-1/pass-2 routines (LightSeq inference article, hierarchical decoding):
+
+* every piece's threshold equals the oracle's R-top-k of that piece under the
+  documented partition (element e of the aligned frame in group e mod
+  ngroups) -- bit for bit, since max/min are exact -- and never exceeds the
+  piece's k-th largest logit;
+* every piece's hit count equals the number of its logits >= threshold;
+* each batch element's queue holds exactly those survivors (or the piece's
+  exact top-k when it overflowed);
+* the merged log-sum-exp matches the oracle's float64 value;
+* for i.i.d. rows the mean number of survivors per piece matches the
+  inclusion-exclusion expectation.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from beam_search_top_amd import rtopk, synth
+from gpu_util import DEV, misaligned_copy, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _as_f32(s):
+    if s.dtype == synth.BF16:
+        return synth.bf16_bits_to_f32(s.logits)
+    return s.logits.astype(np.float32)
+
+
+def piece_ranges(plan, row, V, align):
+    epv, vpc = plan["elems_per_vec"], plan["vecs_per_chunk"]
+    e0 = row * V + align
+    v0 = e0 // epv
+    lead = e0 - v0 * epv
+    span = (lead + V + epv - 1) // epv
+    out = []
+    for c in range(plan["chunks"]):
+        lo = max(0, c * vpc * epv - lead)
+        hi = min(V, min((c + 1) * vpc, span) * epv - lead)
+        out.append((lo, max(lo, hi), (e0 + lo) % plan["ngroups"]))
+    return out
+
+
+def run_debug(s, x=None):
+    if x is None:
+        x, a, f = to_device(s)
+    else:
+        a, f = torch.from_numpy(s.alive).to(DEV), torch.from_numpy(s.finished).to(DEV)
+    d = rtopk.debug_step(x, a, f, k=s.k, eos_id=s.eos_id)
+    torch.cuda.synchronize()
+    align = (x.data_ptr() % 16) // x.element_size()
+    return {k: (v.cpu().numpy() if torch.is_tensor(v) else v) for k, v in d.items()}, align
+
+
+def check_intermediates(s, d, align):
+    plan = d["plan"]
+    C, k, V = plan["chunks"], s.k, s.V
+    x32 = _as_f32(s)
+    ref_lse = oracle.lse(s.logits, s.dtype).reshape(-1)
+    n_over = 0
+    for b in range(s.B):
+        want = []
+        for j in range(s.beam):
+            row = b * s.beam + j
+            if s.finished[b, j]:
+                assert np.isnan(d["lse"][row])
+                continue
+            assert abs(float(d["lse"][row]) - ref_lse[row]) <= 4e-6 * max(1.0, abs(ref_lse[row])), (b, j)
+            rowx = s.logits[b, j]
+            for c, (lo, hi, off) in enumerate(piece_ranges(plan, row, V, align)):
+                u = row * C + c
+                T = float(d["T"][u])
+                if hi <= lo:
+                    assert T == -math.inf and d["hits"][u] == 0
+                    continue
+                T_ref = oracle.threshold(rowx, s.dtype, plan["ngroups"], k, offset=off, base=lo, n=hi - lo)
+                assert T == T_ref, (b, j, c, T, T_ref)
+                seg = x32[b, j, lo:hi].astype(np.float64)
+                if hi - lo >= k:
+                    assert T <= np.sort(seg)[::-1][k - 1]  # R-top-k never exceeds the k-th largest
+                hits = oracle.count_ge(rowx, s.dtype, T, base=lo, n=hi - lo)
+                assert int(d["hits"][u]) == hits, (b, j, c)
+                ts = np.arange(lo, hi)
+                if hits <= plan["chunk_limit"]:
+                    sel = ts[seg >= T]
+                else:
+                    n_over += 1
+                    order = np.lexsort((ts, -seg))[:k]
+                    sel = ts[order]
+                for t in sel:
+                    xv = np.float32(x32[b, j, t] + np.float32(0.0)) if hits > plan["chunk_limit"] else x32[b, j, t]
+                    want.append((int(np.array(xv, np.float32).view(np.uint32)) << 32) | (j * V + int(t)))
+        n = int(d["count"][b])
+        got = sorted(int(v) & 0xFFFFFFFFFFFFFFFF for v in d["queue"][b, :n])
+        assert got == sorted(want), (b, n, len(want))
+    return n_over
+
+
+@pytest.mark.parametrize("name", ["tiny", "c32k", "spiked40k", "b128"])
+def test_intermediates_configs(name):
+    s = synth.make_step(name)
+    d, align = run_debug(s)
+    check_intermediates(s, d, align)
+
+
+def test_intermediates_mixed250k_sample():
+    s = synth.make_step("mixed250k")
+    d, align = run_debug(s)
+    # the full check is slow in Python; check 6 batch elements exhaustively
+    sub = synth.Step(name="mixed_sub", B=6, beam=s.beam, k=s.k, V=s.V, dtype=s.dtype,
+                     logits=s.logits[:6], alive=s.alive[:6], finished=s.finished[:6])
+    dsub = dict(d)
+    C = d["plan"]["chunks"]
+    dsub["T"], dsub["hits"] = d["T"][:6 * s.beam * C], d["hits"][:6 * s.beam * C]
+    dsub["lse"], dsub["count"], dsub["queue"] = d["lse"][:6 * s.beam], d["count"][:6], d["queue"][:6]
+    check_intermediates(sub, dsub, align)
+
+
+@pytest.mark.parametrize("offset", [0, 3])
+def test_intermediates_ragged_and_misaligned(offset):
+    s = synth.make_custom(3, 4, 3, 10001, synth.F16, seed=8, sigma=3.0, n_finished=1)
+    x = misaligned_copy(s, offset) if offset else None
+    d, align = run_debug(s, x)
+    assert align == offset
+    check_intermediates(s, d, align)
+
+
+def test_intermediates_overflow():
+    s = synth.make_custom(2, 4, 4, 30000, synth.F16, seed=9, dist="int")
+    assert rtopk.rtopk_set_override(0, 16) == 0
+    try:
+        d, align = run_debug(s)
+    finally:
+        rtopk.rtopk_set_override(0, 0)
+    assert check_intermediates(s, d, align) > 0  # some pieces took the exact top-k path
+
+
+def _expected_survivors(n, k):
+    """E[#{x >= R-top-k}] for n i.i.d. continuous values in k equal groups."""
+    g = n // k
+    total, j = 0.0, 0
+    while True:
+        p = 0.0
+        for i in range(1, k + 1):
+            ratio = 1.0
+            for m in range(j):
+                ratio *= (n - i * g - m) / (n - m)
+            p += (-1) ** (i + 1) * math.comb(k, i) * ratio
+        total += p
+        if p < 1e-12 or j > n:
+            return total
+        j += 1
+
+
+def test_survivor_statistics_match_closed_form():
+    s = synth.make_custom(64, 4, 4, 40000, synth.F32, seed=10, sigma=3.0)
+    d, align = run_debug(s)
+    plan = d["plan"]
+    sizes = {}
+    for row in range(s.B * s.beam):
+        for c, (lo, hi, _) in enumerate(piece_ranges(plan, row, s.V, align)):
+            sizes.setdefault(hi - lo, []).append(int(d["hits"][row * plan["chunks"] + c]))
+    for n, hits in sizes.items():
+        if len(hits) < 50 or n % 4:
+            continue
+        hits = np.array(hits, float)
+        exp = _expected_survivors(n, 4)
+        assert abs(hits.mean() - exp) < 5 * hits.std() / math.sqrt(len(hits)) + 1e-9, (n, hits.mean(), exp)

@@ -1,0 +1,196 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Indices must match bit for bit except at near-ties; scores within 1e-5
+relative for float32 logits and 2e-3 for float16/bfloat16 (floor 1), the rule
+in tests/compare.py. Workloads are the five seeded configurations at full size
+plus edge cases: ragged and misaligned rows, tiny vocabularies, k = V, k = 1,
+non-power-of-two k, k = 64, every beam finished, exact ties, -inf logits,
+forced per-piece overflow, every register-tile variant, the caller-workspace
+entry point, and bit-exact repeatability.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from beam_search_top_amd import rtopk, synth
+from compare import compare
+from gpu_util import DEV, misaligned_copy, run, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def check(s, got, nthreads=8):
+    ref = oracle.step_of(s, nthreads=nthreads)
+    problems = compare(s, got[0], got[1], got[2], ref)
+    assert not problems, f"{s.name} seed={s.seed}:\n" + "\n".join(problems)
+    return ref
+
+
+@pytest.mark.parametrize("name", ["tiny", "c32k", "spiked40k", "b128"])
+@pytest.mark.parametrize("seed_off", [0, 1, 2])
+def test_configs(name, seed_off):
+    s = synth.make_step(name, synth.default_seed(name) + 100 * seed_off)
+    print(f"[parity] {name} seed={s.seed}", flush=True)
+    check(s, run(s))
+
+
+def test_config_mixed250k():
+    s = synth.make_step("mixed250k")
+    print(f"[parity] mixed250k seed={s.seed}", flush=True)
+    check(s, run(s), nthreads=16)
+
+
+def test_tiny_against_exact_indices():
+    s = synth.make_step("tiny")
+    got = run(s)
+    ref = oracle.step_of(s)
+    assert np.array_equal(got[0], ref.beam_ids) and np.array_equal(got[1], ref.token_ids)
+
+
+EDGE = [
+    # B, beam, k, V, dtype, kwargs
+    (3, 4, 4, 1001, synth.F16, {}),                  # ragged rows: V*2 bytes not a multiple of 16
+    (2, 3, 3, 37, synth.F32, {}),                    # tiny ragged vocabulary, k = 3 (8 groups... 4)
+    (2, 2, 2, 3, synth.BF16, {}),                    # V < vector width
+    (1, 1, 4, 4, synth.F32, {}),                     # k = V = beam*V
+    (5, 1, 7, 700, synth.F16, {}),                   # beam = 1, odd k
+    (1, 6, 1, 5000, synth.BF16, {}),                 # k = 1, B = 1
+    (2, 16, 64, 5000, synth.F16, {}),                # k = 64 (max), ngroups 64
+    (3, 5, 5, 2999, synth.F32, {"n_finished": 4}),   # k = 5 -> 8 groups, finished beams
+    (4, 3, 3, 40000, synth.BF16, {"dist": "gumbel"}),
+    (2, 4, 4, 40000, synth.F16, {"dist": "int"}),    # small integers: heavy exact ties
+    (2, 4, 4, 40000, synth.F16, {"sigma": 20000.0}), # large magnitudes
+    (2, 8, 8, 100000, synth.F32, {"dist": "uniform", "sigma": 0.001}),
+    (1, 2, 2, 8, synth.F32, {"n_finished": 1}),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[f"{c[0]}x{c[1]}x{c[3]}k{c[2]}d{c[4]}" for c in EDGE])
+def test_edge_shapes(case):
+    B, beam, k, V, dt, kw = case
+    s = synth.make_custom(B, beam, k, V, dt, seed=4242 + V + k, **kw)
+    s.eos_id = min(2, V - 1)
+    print(f"[parity] {s.name}", flush=True)
+    check(s, run(s))
+
+
+def test_all_finished_pads():
+    s = synth.make_custom(3, 2, 5, 50, synth.F16, seed=7, n_finished=6)
+    got = run(s)
+    ref = check(s, got)
+    assert (got[0][:, 2:] == -1).all() and (got[1][:, 2:] == -1).all()
+    assert np.isneginf(got[2][:, 2:]).all()
+    assert np.array_equal(got[2][:, :2], ref.scores[:, :2])  # frozen scores, bit-exact
+
+
+def test_constant_rows_tie_break_bf16():
+    s = synth.make_custom(4, 8, 8, 250000, synth.BF16, seed=3, const=1.0)
+    s.alive[:] = -2.5  # all beams tie too: pure flat-index order
+    got = run(s)
+    check(s, got)
+    assert (got[0] == 0).all() and (got[1] == np.arange(8)[None, :]).all()
+
+
+def test_duplicate_beams_tie_by_flat_index():
+    s = synth.make_custom(3, 4, 4, 40000, synth.F16, seed=12, sigma=3.0)
+    s.logits[:, 2] = s.logits[:, 0]
+    s.alive[:, 2] = s.alive[:, 0]
+    got = run(s)
+    check(s, got)
+    # identical rows must get identical scores on the GPU (deterministic lse)
+    for b in range(3):
+        for p in range(4):
+            if got[0][b, p] == 2:
+                q = np.where((got[0][b] == 0) & (got[1][b] == got[1][b, p]))[0]
+                if len(q):
+                    assert got[2][b, q[0]] == got[2][b, p]
+
+
+def test_neg_inf_logits():
+    s = synth.make_custom(2, 4, 4, 3000, synth.F32, seed=99, sigma=2.0)
+    rng = np.random.default_rng(5)
+    mask = rng.random(s.logits.shape) < 0.5
+    s.logits[mask] = -np.inf
+    check(s, run(s))
+
+
+@pytest.mark.parametrize("offset", [1, 3, 5, 7])
+def test_misaligned_base_pointer(offset):
+    s = synth.make_custom(4, 4, 4, 4096, synth.F16, seed=21 + offset, sigma=3.0, n_finished=2)
+    x = misaligned_copy(s, offset)
+    a = torch.from_numpy(s.alive).to(DEV)
+    f = torch.from_numpy(s.finished).to(DEV)
+    assert x.data_ptr() % 16 != 0
+    out = rtopk.beam_step(x, a, f, k=s.k, eos_id=s.eos_id)
+    torch.cuda.synchronize()
+    check(s, [o.cpu().numpy() for o in out])
+
+
+def test_forced_overflow_path_is_exact():
+    # chunk limit 1 (raised to k): every piece with more than k candidates emits its exact top-k
+    cases = [synth.make_step("b128"), synth.make_custom(2, 8, 8, 250000, synth.BF16, seed=5, const=1.0),
+             synth.make_custom(3, 4, 4, 40000, synth.F16, seed=6, dist="int")]
+    assert rtopk.rtopk_set_override(0, 1) == 0
+    try:
+        for s in cases:
+            print(f"[parity overflow] {s.name}", flush=True)
+            check(s, run(s))
+    finally:
+        rtopk.rtopk_set_override(0, 0)
+
+
+@pytest.mark.parametrize("nv", [1, 2, 3, 4, 6, 8, 10, 12, 16])
+def test_every_tile_variant(nv):
+    cases = [synth.make_custom(4, 4, 4, 40000, synth.F16, seed=300 + nv, sigma=3.0, n_finished=1),
+             synth.make_custom(2, 4, 4, 32000, synth.F32, seed=400 + nv, sigma=2.0),
+             synth.make_custom(2, 8, 8, 50000, synth.BF16, seed=500 + nv, dist="gumbel"),
+             synth.make_custom(2, 3, 3, 20001, synth.F16, seed=600 + nv, sigma=3.0)]
+    assert rtopk.rtopk_set_override(nv, 0) == 0
+    try:
+        for s in cases:
+            check(s, run(s))
+    finally:
+        rtopk.rtopk_set_override(0, 0)
+
+
+def test_workspace_entry_point_matches_and_reuses():
+    s1 = synth.make_step("b128")
+    s2 = synth.make_custom(5, 4, 4, 40000, synth.F16, seed=77, n_finished=2)
+    nbytes = max(rtopk.rtopk_workspace_bytes(s.B, s.beam, s.V, s.k, s.dtype) for s in (s1, s2))
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    for s in (s1, s2, s1):
+        x, a, f = to_device(s)
+        plain = rtopk.beam_step(x, a, f, k=s.k)
+        with_ws = rtopk.beam_step(x, a, f, k=s.k, workspace=ws)
+        torch.cuda.synchronize()
+        for p, w in zip(plain, with_ws):
+            assert torch.equal(p, w)
+        check(s, [o.cpu().numpy() for o in with_ws])
+
+
+def test_repeatable_bit_for_bit():
+    s = synth.make_step("b128")
+    x, a, f = to_device(s)
+    first = [o.clone() for o in rtopk.beam_step(x, a, f, k=s.k)]
+    for _ in range(20):
+        again = rtopk.beam_step(x, a, f, k=s.k)
+        for p, q in zip(first, again):
+            assert torch.equal(p, q)
+    torch.cuda.synchronize()
+
+
+def test_streams_have_separate_workspaces():
+    s = synth.make_step("b128")
+    x, a, f = to_device(s)
+    ref = [o.clone() for o in rtopk.beam_step(x, a, f, k=s.k)]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    outs = []
+    for st in streams:
+        with torch.cuda.stream(st):
+            outs.append(rtopk.beam_step(x, a, f, k=s.k))
+    torch.cuda.synchronize()
+    for o in outs:
+        for p, q in zip(ref, o):
+            assert torch.equal(p, q)
