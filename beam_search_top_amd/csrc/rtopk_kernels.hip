@@ -37,11 +37,17 @@
 //    threshold max_c T_c and the batch bound S = max_j (alive_j + T_j -
 //    lse_j) (at least k candidates score >= S), and sorts the survivors with
 //    an LDS bitonic network on 64-bit keys (score desc, flat index asc).
-//    It then resets the queue counter and the ticket for the next call.
+//    It then zeroes everything its batch element used in the workspace
+//    (queue entries, partials, counter, ticket): between calls the workspace
+//    is all-zero, whatever the shapes of the calls that share it.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include "rtopk_internal.h"
+
+// No implicit a*b+c contraction: a score and the bound it is compared with
+// must round identically (explicit fmaf calls still map to FMA instructions).
+#pragma clang fp contract(off)
 
 namespace rtopk {
 namespace {
@@ -717,10 +723,19 @@ __device__ void sort_batch(const StepArgs &a, SortSmem &sm, int b, int tid)
     if (a.dbg_queue)
         for (uint32_t e = tid; e < n; e += kThreads)
             a.dbg_queue[(long long)b * a.queue_cap + e] = q[e];
+    // Leave every workspace byte this batch element used at zero, so the
+    // workspace is all-zero between calls whatever shape comes next. Each
+    // thread clears only queue entries it read itself; the partials were read
+    // before the barriers above.
+    uint64_t *qw = a.queue + (long long)b * a.queue_cap;
+    for (uint32_t e = tid; e < n; e += kThreads)
+        qw[e] = 0ull;
+    for (int u = tid; u < beam * C; u += kThreads)
+        a.part[(long long)b * beam * C + u] = make_float4(0.f, 0.f, 0.f, 0.f);
     if (tid == 0) {
         if (a.dbg_count)
             a.dbg_count[b] = n;
-        a.count[b] = 0u; // leave the workspace ready for the next call
+        a.count[b] = 0u;
         a.ticket[b] = 0u;
     }
 }

@@ -119,9 +119,10 @@ size_t rtopk_workspace_bytes(int B, int beam, int V, int k, int dtype);
 /*
  * rtopk_beam_step with a caller-owned device workspace of ws_bytes >=
  * rtopk_workspace_bytes(...) bytes, 256-byte aligned. It must be zero-filled
- * before its first use; every completed call leaves it ready for the next, for
- * any shape that fits. Calls sharing one workspace must be ordered (same
- * stream). Allocates nothing. RTOPK_ENOMEM when ws_bytes is too small.
+ * before its first use; every completed call leaves it all-zero again, so it
+ * serves any later call whose shape fits. Calls sharing one workspace must be
+ * ordered (same stream). Allocates nothing. RTOPK_ENOMEM when ws_bytes is too
+ * small.
  */
 int rtopk_beam_step_ws(const void *logits, int dtype, const float *alive_scores,
                        const uint8_t *finished_mask, int B, int beam, int V, int k, int eos_id,
