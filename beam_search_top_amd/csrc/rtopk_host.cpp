@@ -38,11 +38,11 @@ int fail(int status, const char *fmt, ...)
 std::atomic<int> g_override_nv{0};
 std::atomic<int> g_override_limit{0};
 
-const int kVecsPerThread[] = {1, 2, 3, 4, 6, 8, 10, 12, 16};
-// Most 16-byte vectors a thread holds without exceeding ~160 VGPRs (no
-// spills, >= 3 waves per SIMD): fp16 keeps its max on packed pairs and
-// needs fewer registers per vector than fp32 and bf16.
-int max_vecs_per_thread(int dtype) { return dtype == RTOPK_F16 ? 16 : 12; }
+const int kVecsPerThread[] = {1, 2, 3, 4, 6, 8, 10, 12};
+// Most 16-byte vectors a thread holds without register spills and with >= 4
+// waves per SIMD; rows that share vectors with their neighbours need the
+// element-wise masking code and get fewer.
+int max_vecs_per_thread(bool aligned_rows) { return aligned_rows ? 12 : 10; }
 // Workgroups wanted per launch before pieces are made smaller: 4 per CU on 256 CUs.
 constexpr long long kTargetGrid = 1024;
 
@@ -90,7 +90,7 @@ int make_plan(const void *logits, int B, int beam, int V, int k, int dtype, rtop
     if (nv > 0) {
         C = ceil_div(span, (long long)rtopk::kThreads * nv);
     } else {
-        const int nvmax = max_vecs_per_thread(dtype);
+        const int nvmax = max_vecs_per_thread(aligned_rows);
         const long long c0 = ceil_div(span, (long long)rtopk::kThreads * nvmax);
         C = c0;
         if (rows * c0 < kTargetGrid) {
@@ -122,19 +122,24 @@ int make_plan(const void *logits, int B, int beam, int V, int k, int dtype, rtop
     p->grid = rows * C;
     if (p->grid > INT_MAX)
         return fail(RTOPK_ENOTSUP, "grid of %lld workgroups is too large", p->grid);
-    const long long qcap = (long long)beam * C * p->chunk_limit;
+    if ((long long)beam * C > rtopk::kMaxPieces)
+        return fail(RTOPK_ENOTSUP, "beam*chunks = %lld exceeds the implementation limit %d (vocabulary too large "
+                    "for this beam count)", (long long)beam * C, rtopk::kMaxPieces);
+    const long long qcap = (long long)beam * C * k; // every piece publishes at most its top-k
     if (qcap > INT_MAX)
         return fail(RTOPK_ENOTSUP, "candidate queue of %lld entries is too large", qcap);
     p->queue_cap = (int)qcap;
 
+    if (B > rtopk::kTicketCap)
+        return fail(RTOPK_ENOTSUP, "B=%d exceeds the implementation limit %d", B, rtopk::kTicketCap);
+    // tickets first, in a region of fixed size: no shape ever stores other
+    // data there, so it stays zero between calls whatever the shapes are
     size_t off = 0;
-    p->ws_count_off = off;
-    off = align256(off + sizeof(uint32_t) * (size_t)B);
     p->ws_ticket_off = off;
-    off = align256(off + sizeof(uint32_t) * (size_t)B);
-    p->ws_part_off = off;
+    off = align256(off + sizeof(uint32_t) * (size_t)rtopk::kTicketCap);
+    p->ws_head_off = off;
     off = align256(off + 16 * (size_t)rows * (size_t)C);
-    p->ws_queue_off = off;
+    p->ws_slots_off = off;
     off = align256(off + sizeof(uint64_t) * (size_t)B * (size_t)p->queue_cap);
     p->ws_bytes = off;
     return RTOPK_OK;
@@ -180,10 +185,9 @@ int enqueue(const rtopk::Plan &p, const void *logits, int dtype, const float *al
     a.chunk_limit = p.chunk_limit;
     a.queue_cap = p.queue_cap;
     uint8_t *w = (uint8_t *)ws;
-    a.count = (uint32_t *)(w + p.ws_count_off);
     a.ticket = (uint32_t *)(w + p.ws_ticket_off);
-    a.part = (float4 *)(w + p.ws_part_off);
-    a.queue = (uint64_t *)(w + p.ws_queue_off);
+    a.head = (uint64_t *)(w + p.ws_head_off);
+    a.slots = (uint64_t *)(w + p.ws_slots_off);
     a.out_beam = ob;
     a.out_token = ot;
     a.out_score = os;

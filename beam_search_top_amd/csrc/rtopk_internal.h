@@ -8,10 +8,12 @@
 namespace rtopk {
 
 constexpr int kThreads = 256;       // threads per workgroup (4 wave64s)
-constexpr int kMaxChunkLimit = 256; // LDS staging slots for one piece's candidates
-constexpr int kSortTile = 2048;     // LDS keys the per-batch sort handles in one tile
-constexpr int kMaxBeam = 512;       // per-beam LDS tables of the per-batch sort
+constexpr int kMaxChunkLimit = 256; // candidate slots of one piece (LDS stage and workspace)
+constexpr int kSortKeys = 1024;     // LDS keys the per-batch selection sorts in one pass
+constexpr int kMaxPieces = 2048;    // pieces (beam * chunks) of one batch element
+constexpr int kMaxBeam = 512;       // per-beam LDS tables of the per-batch selection
 constexpr int kMaxK = 64;
+constexpr int kTicketCap = 65536;   // batch elements the ticket region holds (B limit)
 
 // Everything one launch needs, passed by value as the kernel argument.
 struct StepArgs {
@@ -23,13 +25,12 @@ struct StepArgs {
     int chunks;                    // pieces per row
     int vecs_per_chunk;            // 16-byte vectors per piece
     int ngroups;                   // groups of the threshold pass (power of two >= k)
-    int chunk_limit;               // >= k, <= kMaxChunkLimit
-    int queue_cap;                 // queue entries per batch element
-    // workspace
-    uint32_t *count;               // [B] queue fill
-    uint32_t *ticket;              // [B] arrivals
-    float4 *part;                  // [B*beam*chunks] (max2, sum, threshold, 0)
-    uint64_t *queue;               // [B*queue_cap]
+    int chunk_limit;               // >= k, <= kMaxChunkLimit: candidates a piece stages in LDS
+    int queue_cap;                 // candidate slots per batch element = beam*chunks*k
+    // workspace; only the ticket region must be zero when a call starts
+    uint32_t *ticket;              // [kTicketCap] arrivals, first B used
+    uint64_t *head;                // [B*beam*chunks][2]: (max2 | sum << 32), (threshold | count << 32)
+    uint64_t *slots;               // [B*beam*chunks][k] each piece's top-k sort keys by logit
     // outputs
     int32_t *out_beam, *out_token;
     float *out_score;
@@ -46,7 +47,7 @@ struct Plan {
     int chunks, vecs_per_thread, vecs_per_chunk;
     int ngroups, chunk_limit, queue_cap, align_elems;
     long long grid;
-    size_t ws_count_off, ws_ticket_off, ws_part_off, ws_queue_off, ws_bytes;
+    size_t ws_ticket_off, ws_head_off, ws_slots_off, ws_bytes;
 };
 
 // Enqueue the fused select + sort kernel. Returns a hipError_t.

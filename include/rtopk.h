@@ -58,7 +58,8 @@ typedef enum { RTOPK_F32 = 0, RTOPK_F16 = 1, RTOPK_BF16 = 2 } rtopk_dtype;
 typedef enum {
     RTOPK_OK = 0,
     RTOPK_EINVAL = -1,  /* bad argument: NULL pointer, size < 1, k > beam*V, eos outside [0,V), ... */
-    RTOPK_ENOTSUP = -2, /* valid but beyond the implementation limits: k > 64, beam > 512 */
+    RTOPK_ENOTSUP = -2, /* valid but beyond the implementation limits: k > 64, beam > 512,
+                           B > 65536, beam * pieces-per-row > 2048 */
     RTOPK_ENOMEM = -3,  /* device allocation failed, or a caller workspace is too small */
     RTOPK_EHIP = -4     /* a HIP runtime call or kernel launch failed */
 } rtopk_status;
@@ -75,9 +76,11 @@ typedef enum {
  * piece, element e (counted from the 16-byte-aligned address at or below the
  * logits base pointer) belongs to group e mod `ngroups`; ngroups is k rounded
  * up to a power of two and the piece's threshold is the k-th largest group
- * maximum (the minimum when ngroups == k). A piece with more than
- * `chunk_limit` logits at or above its threshold emits only its own exact
- * top-k; `queue_cap` is the candidate-queue length per batch element.
+ * maximum (the minimum when ngroups == k). Each piece publishes only its own
+ * exact top-k by (logit desc, flat index asc) among the logits at or above its
+ * threshold; up to `chunk_limit` of those are ranked in LDS, a piece with more
+ * finds its top-k by k rounds of argmax. `queue_cap` = beam * chunks * k is the
+ * candidate count per batch element.
  */
 typedef struct {
     int chunks;          /* pieces per beam row (C) */
@@ -86,8 +89,8 @@ typedef struct {
     int vecs_per_chunk;  /* 16-byte vectors per piece */
     int elems_per_vec;   /* 4 for float32, 8 for float16/bfloat16 */
     int ngroups;         /* groups of the threshold pass */
-    int chunk_limit;     /* candidates a piece may emit before switching to its exact top-k */
-    int queue_cap;       /* candidate-queue entries per batch element */
+    int chunk_limit;     /* candidates a piece ranks in LDS before switching to k argmax rounds */
+    int queue_cap;       /* candidate slots per batch element (beam * chunks * k) */
     int align_elems;     /* misalignment of the logits base, in elements */
     int grid;            /* workgroups launched: B * beam * chunks */
 } rtopk_plan_t;
@@ -119,10 +122,11 @@ size_t rtopk_workspace_bytes(int B, int beam, int V, int k, int dtype);
 /*
  * rtopk_beam_step with a caller-owned device workspace of ws_bytes >=
  * rtopk_workspace_bytes(...) bytes, 256-byte aligned. It must be zero-filled
- * before its first use; every completed call leaves it all-zero again, so it
- * serves any later call whose shape fits. Calls sharing one workspace must be
- * ordered (same stream). Allocates nothing. RTOPK_ENOMEM when ws_bytes is too
- * small.
+ * before its first use; every completed call leaves it ready for any later
+ * call whose shape fits (its first 256 KiB, the arrival counters, are zero
+ * again after each call; the rest holds scratch data). Calls sharing one
+ * workspace must be ordered (same stream). Allocates nothing. RTOPK_ENOMEM
+ * when ws_bytes is too small.
  */
 int rtopk_beam_step_ws(const void *logits, int dtype, const float *alive_scores,
                        const uint8_t *finished_mask, int B, int beam, int V, int k, int eos_id,
@@ -132,11 +136,13 @@ int rtopk_beam_step_ws(const void *logits, int dtype, const float *alive_scores,
 /*
  * rtopk_beam_step_ws that also copies out intermediate values (for tests):
  *   dbg_T       device [B*beam*chunks] float32: each piece's threshold (-inf if empty)
- *   dbg_hits    device [B*beam*chunks] uint32: logits >= threshold in the piece
+ *   dbg_hits    device [B*beam*chunks] uint32: logits >= threshold in the piece (its
+ *               R-top-k survivors, of which it publishes the best min(hits, k))
  *   dbg_lse     device [B*beam] float32: merged log-sum-exp (NaN for finished beams)
- *   dbg_count   device [B] uint32: candidate-queue entries of each batch element
- *   dbg_queue   device [B*queue_cap] uint64: the queue, entry = (float32 bits of the
- *               logit << 32) | (j*V + t); only the first dbg_count[b] are defined
+ *   dbg_count   device [B] uint32: candidates the pieces of each batch element emitted
+ *   dbg_queue   device [B*queue_cap] uint64: those candidates, entry = (float32 bits of
+ *               the logit << 32) | (j*V + t), in no particular order; only the first
+ *               dbg_count[b] of each batch element are defined
  * Any debug pointer may be NULL. Finished beams leave their dbg_T/dbg_hits unset.
  */
 int rtopk_debug_step(const void *logits, int dtype, const float *alive_scores,
@@ -154,9 +160,10 @@ int rtopk_plan(const void *logits, int B, int beam, int V, int k, int dtype, rto
 /*
  * Process-wide tuning overrides for experiments and tests (0 = automatic):
  * vecs_per_thread forces the 16-byte vectors each thread holds (one of
- * 1,2,3,4,6,8,10,12,16; others are rejected with RTOPK_EINVAL);
- * chunk_limit forces the per-piece candidate limit (1..256), which makes the
- * exact per-piece top-k path run whenever a piece has more candidates.
+ * 1,2,3,4,6,8,10,12; others are rejected with RTOPK_EINVAL);
+ * chunk_limit forces the per-piece LDS candidate limit (1..256, raised to k),
+ * which makes the argmax-rounds top-k path run whenever a piece has more
+ * candidates.
  */
 int rtopk_set_override(int vecs_per_thread, int chunk_limit);
 

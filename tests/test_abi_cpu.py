@@ -111,7 +111,7 @@ def test_plan_covers_rows(lib, shape):
         assert p.grid == B * beam * p.chunks
         assert p.ngroups >= k and p.ngroups & (p.ngroups - 1) == 0 and p.ngroups < 2 * k
         assert p.chunk_limit >= k
-        assert p.queue_cap == beam * p.chunks * p.chunk_limit
+        assert p.queue_cap == beam * p.chunks * k
         need = rtopk.rtopk_workspace_bytes(B, beam, V, k, dt)
         assert need >= 8 * B * p.queue_cap + 16 * B * beam * p.chunks
 

@@ -6,8 +6,8 @@ pass-1/pass-2 routines (LightSeq inference article, hierarchical decoding):
   ngroups) -- bit for bit, since max/min are exact -- and never exceeds the
   piece's k-th largest logit;
 * every piece's hit count equals the number of its logits >= threshold;
-* each batch element's queue holds exactly those survivors (or the piece's
-  exact top-k when it overflowed);
+* each piece publishes exactly its own top-min(hits, k) survivors by
+  (logit desc, flat asc);
 * the merged log-sum-exp matches the oracle's float64 value;
 * for i.i.d. rows the mean number of survivors per piece matches the
   inclusion-exclusion expectation.
@@ -85,14 +85,13 @@ def check_intermediates(s, d, align):
                 hits = oracle.count_ge(rowx, s.dtype, T, base=lo, n=hi - lo)
                 assert int(d["hits"][u]) == hits, (b, j, c)
                 ts = np.arange(lo, hi)
-                if hits <= plan["chunk_limit"]:
-                    sel = ts[seg >= T]
-                else:
+                if hits > plan["chunk_limit"]:
                     n_over += 1
-                    order = np.lexsort((ts, -seg))[:k]
-                    sel = ts[order]
+                # every piece publishes its own top-min(hits, k) by (logit desc, flat asc)
+                sel = ts[np.lexsort((ts, -seg))[:min(hits, k)]]
+                assert (seg[sel - lo] >= T).all()
                 for t in sel:
-                    xv = np.float32(x32[b, j, t] + np.float32(0.0)) if hits > plan["chunk_limit"] else x32[b, j, t]
+                    xv = np.float32(x32[b, j, t] + np.float32(0.0))
                     want.append((int(np.array(xv, np.float32).view(np.uint32)) << 32) | (j * V + int(t)))
         n = int(d["count"][b])
         got = sorted(int(v) & 0xFFFFFFFFFFFFFFFF for v in d["queue"][b, :n])

@@ -58,6 +58,8 @@ EDGE = [
     (1, 6, 1, 5000, synth.BF16, {}),                 # k = 1, B = 1
     (2, 16, 64, 5000, synth.F16, {}),                # k = 64 (max), ngroups 64
     (3, 5, 5, 2999, synth.F32, {"n_finished": 4}),   # k = 5 -> 8 groups, finished beams
+    (1, 32, 8, 250000, synth.BF16, {}),              # 352 pieces per batch element (> 256 threads)
+    (2, 8, 8, 250000, synth.BF16, {"dist": "uniform", "sigma": 0.001}),  # ~70 ties per piece
     (4, 3, 3, 40000, synth.BF16, {"dist": "gumbel"}),
     (2, 4, 4, 40000, synth.F16, {"dist": "int"}),    # small integers: heavy exact ties
     (2, 4, 4, 40000, synth.F16, {"dist": "uniform", "sigma": 60000.0}),  # large finite magnitudes
@@ -140,7 +142,7 @@ def test_forced_overflow_path_is_exact():
         rtopk.rtopk_set_override(0, 0)
 
 
-@pytest.mark.parametrize("nv", [1, 2, 3, 4, 6, 8, 10, 12, 16])
+@pytest.mark.parametrize("nv", [1, 2, 3, 4, 6, 8, 10, 12])
 def test_every_tile_variant(nv):
     cases = [synth.make_custom(4, 4, 4, 40000, synth.F16, seed=300 + nv, sigma=3.0, n_finished=1),
              synth.make_custom(2, 4, 4, 32000, synth.F32, seed=400 + nv, sigma=2.0),
@@ -205,16 +207,18 @@ def test_library_workspace_survives_shape_changes():
         check(s, run(s))
 
 
-def test_caller_workspace_is_all_zero_after_each_call():
+def test_caller_workspace_tickets_return_to_zero():
+    # Only the arrival counters (the first 256 KiB) must be zero between calls;
+    # calls of different shapes then share one caller workspace.
     s_small = synth.make_custom(3, 4, 4, 40000, synth.F16, seed=31, n_finished=1)
     s_big = synth.make_step("b128")
     nbytes = rtopk.rtopk_workspace_bytes(s_big.B, s_big.beam, s_big.V, s_big.k, s_big.dtype)
     ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
-    for s in (s_small, s_big, s_small):
+    for s in (s_small, s_big, s_small, s_big):
         x, a, f = to_device(s)
         out = rtopk.beam_step(x, a, f, k=s.k, workspace=ws)
         torch.cuda.synchronize()
-        assert int(torch.count_nonzero(ws)) == 0
+        assert int(torch.count_nonzero(ws[:256 * 1024])) == 0
         check(s, [o.cpu().numpy() for o in out])
 
 
