@@ -39,12 +39,16 @@ std::atomic<int> g_override_nv{0};
 std::atomic<int> g_override_limit{0};
 
 const int kVecsPerThread[] = {1, 2, 3, 4, 6, 8, 10, 12};
-// Most 16-byte vectors a thread holds without register spills and with >= 4
+// Most 16-byte vectors a lane holds without register spills and with >= 4
 // waves per SIMD; rows that share vectors with their neighbours need the
 // element-wise masking code and get fewer.
-int max_vecs_per_thread(bool aligned_rows) { return aligned_rows ? 12 : 10; }
-// Workgroups wanted per launch before pieces are made smaller: 4 per CU on 256 CUs.
-constexpr long long kTargetGrid = 1024;
+int max_vecs_per_thread(bool aligned_rows) { return aligned_rows ? 12 : 8; }
+// Waves (one per piece) wanted per launch before pieces are made smaller:
+// 16 per CU on 256 CUs.
+constexpr long long kTargetGrid = 4096;
+constexpr int kMinVecs = 8;
+// Pieces the GPU runs at once: one 16-wave workgroup per CU on 256 CUs.
+constexpr long long kResidentPieces = 4096;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -88,38 +92,43 @@ int make_plan(const void *logits, int B, int beam, int V, int k, int dtype, rtop
     int nv = g_override_nv.load();
     long long C;
     if (nv > 0) {
-        C = ceil_div(span, (long long)rtopk::kThreads * nv);
+        C = ceil_div(span, (long long)rtopk::kLanes * nv);
     } else {
         const int nvmax = max_vecs_per_thread(aligned_rows);
-        const long long c0 = ceil_div(span, (long long)rtopk::kThreads * nvmax);
+        const long long c0 = ceil_div(span, (long long)rtopk::kLanes * nvmax);
         C = c0;
         if (rows * c0 < kTargetGrid) {
             long long want = ceil_div(kTargetGrid, rows);
-            long long cmax = ceil_div(span, rtopk::kThreads); // one vector per thread
+            // no smaller than kMinVecs vectors per lane: past that, more pieces
+            // add per-piece overhead faster than they add memory parallelism
+            long long cmax = ceil_div(span, (long long)rtopk::kLanes * kMinVecs);
             C = want < cmax ? want : cmax;
             if (C < c0)
                 C = c0;
         }
-        const long long need = ceil_div(span, (long long)rtopk::kThreads * C);
+        const long long need = ceil_div(span, (long long)rtopk::kLanes * C);
         nv = nvmax;
         for (int v : kVecsPerThread)
             if (v >= need && v <= nvmax) {
                 nv = v;
                 break;
             }
-        C = ceil_div(span, (long long)rtopk::kThreads * nv);
+        C = ceil_div(span, (long long)rtopk::kLanes * nv);
     }
     p->vecs_per_thread = nv;
     p->chunks = (int)C;
-    // pieces hold exactly threads*nv vectors (so the kernel's unmasked path
+    // pieces hold exactly lanes*nv vectors (so the kernel's unmasked path
     // covers them), except a row's last piece, which holds the remainder
-    p->vecs_per_chunk = rtopk::kThreads * nv;
+    p->vecs_per_chunk = rtopk::kLanes * nv;
     p->ngroups = pow2_ceil(k);
     int lim = g_override_limit.load();
     p->chunk_limit = lim > 0 ? lim : rtopk::kMaxChunkLimit;
     if (p->chunk_limit < k)
         p->chunk_limit = k; // a piece always may emit its own top-k
-    p->grid = rows * C;
+    // Workgroups of 16 pieces while the grid fits the GPU at once (one per
+    // CU), of 4 when workgroups run in rounds and CUs must refill as they go.
+    p->waves = rows * C <= kResidentPieces ? rtopk::kMaxWaves : 4;
+    p->grid = ceil_div(rows * C, p->waves);
     if (p->grid > INT_MAX)
         return fail(RTOPK_ENOTSUP, "grid of %lld workgroups is too large", p->grid);
     if ((long long)beam * C > rtopk::kMaxPieces)
@@ -129,6 +138,16 @@ int make_plan(const void *logits, int B, int beam, int V, int k, int dtype, rtop
     if (qcap > INT_MAX)
         return fail(RTOPK_ENOTSUP, "candidate queue of %lld entries is too large", qcap);
     p->queue_cap = (int)qcap;
+    // LDS of the per-batch selection: sort keys for every published candidate
+    // plus one per finished beam (capped; more survivors take the argmax path),
+    // three float tables per beam, one count byte per piece
+    const long long want_keys = qcap + beam;
+    p->sort_keys = pow2_ceil(want_keys < rtopk::kMaxSortKeys ? (int)want_keys : rtopk::kMaxSortKeys);
+    // sort keys, three floats and a count byte per piece, three floats and a
+    // flag byte per beam
+    const size_t pieces = (size_t)beam * (size_t)C;
+    const size_t sort_lds = 8 * (size_t)p->sort_keys + 13 * pieces + 13 * (size_t)beam;
+    p->lds_bytes = (rtopk::group_lds_bytes(p->waves, sort_lds) + 15) & ~size_t(15);
 
     if (B > rtopk::kTicketCap)
         return fail(RTOPK_ENOTSUP, "B=%d exceeds the implementation limit %d", B, rtopk::kTicketCap);
@@ -184,6 +203,8 @@ int enqueue(const rtopk::Plan &p, const void *logits, int dtype, const float *al
     a.ngroups = p.ngroups;
     a.chunk_limit = p.chunk_limit;
     a.queue_cap = p.queue_cap;
+    a.sort_keys = p.sort_keys;
+    a.waves = p.waves;
     uint8_t *w = (uint8_t *)ws;
     a.ticket = (uint32_t *)(w + p.ws_ticket_off);
     a.head = (uint64_t *)(w + p.ws_head_off);
@@ -196,7 +217,7 @@ int enqueue(const rtopk::Plan &p, const void *logits, int dtype, const float *al
     a.dbg_lse = dbg.lse;
     a.dbg_count = dbg.count;
     a.dbg_queue = dbg.queue;
-    hipError_t e = rtopk::launch_step(a, dtype, p.vecs_per_thread, stream);
+    hipError_t e = rtopk::launch_step(a, dtype, p.vecs_per_thread, p.lds_bytes, stream);
     if (e != hipSuccess)
         return fail(RTOPK_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
     return RTOPK_OK;
@@ -339,7 +360,8 @@ int rtopk_plan(const void *logits, int B, int beam, int V, int k, int dtype, rto
     if (st != RTOPK_OK)
         return st;
     out->chunks = p.chunks;
-    out->threads = rtopk::kThreads;
+    out->threads = rtopk::kLanes;
+    out->pieces_per_group = p.waves;
     out->vecs_per_thread = p.vecs_per_thread;
     out->vecs_per_chunk = p.vecs_per_chunk;
     out->elems_per_vec = p.epv;
@@ -348,6 +370,8 @@ int rtopk_plan(const void *logits, int B, int beam, int V, int k, int dtype, rto
     out->queue_cap = p.queue_cap;
     out->align_elems = p.align_elems;
     out->grid = (int)p.grid;
+    out->sort_keys = p.sort_keys;
+    out->lds_bytes = (int)p.lds_bytes;
     return RTOPK_OK;
 }
 

@@ -3,15 +3,16 @@
 #pragma once
 
 #include <hip/hip_runtime_api.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace rtopk {
 
-constexpr int kThreads = 256;       // threads per workgroup (4 wave64s)
-constexpr int kMaxChunkLimit = 256; // candidate slots of one piece (LDS stage and workspace)
-constexpr int kSortKeys = 1024;     // LDS keys the per-batch selection sorts in one pass
-constexpr int kMaxPieces = 2048;    // pieces (beam * chunks) of one batch element
-constexpr int kMaxBeam = 512;       // per-beam LDS tables of the per-batch selection
+constexpr int kLanes = 64;          // one wave64 per piece
+constexpr int kMaxWaves = 16;       // pieces (waves) per workgroup, at most
+constexpr int kMaxChunkLimit = 64;  // candidates a piece stages in LDS (one per lane)
+constexpr int kMaxSortKeys = 512;   // LDS sort keys of the per-batch selection
+constexpr int kMaxPieces = 3072;    // pieces (beam * chunks) of one batch element (LDS tables)
 constexpr int kMaxK = 64;
 constexpr int kTicketCap = 65536;   // batch elements the ticket region holds (B limit)
 
@@ -27,6 +28,8 @@ struct StepArgs {
     int ngroups;                   // groups of the threshold pass (power of two >= k)
     int chunk_limit;               // >= k, <= kMaxChunkLimit: candidates a piece stages in LDS
     int queue_cap;                 // candidate slots per batch element = beam*chunks*k
+    int sort_keys;                 // LDS sort keys of the per-batch selection (power of two)
+    int waves;                     // pieces (waves) per workgroup, <= kMaxWaves
     // workspace; only the ticket region must be zero when a call starts
     uint32_t *ticket;              // [kTicketCap] arrivals, first B used
     uint64_t *head;                // [B*beam*chunks][2]: (max2 | sum << 32), (threshold | count << 32)
@@ -45,18 +48,23 @@ struct StepArgs {
 struct Plan {
     int elem_bytes, epv;
     int chunks, vecs_per_thread, vecs_per_chunk;
-    int ngroups, chunk_limit, queue_cap, align_elems;
+    int ngroups, chunk_limit, queue_cap, align_elems, sort_keys, waves;
     long long grid;
+    size_t lds_bytes;
     size_t ws_ticket_off, ws_head_off, ws_slots_off, ws_bytes;
 };
 
 // Enqueue the fused select + sort kernel. Returns a hipError_t.
-hipError_t launch_step(const StepArgs &a, int dtype, int vecs_per_thread, hipStream_t stream);
+hipError_t launch_step(const StepArgs &a, int dtype, int vecs_per_thread, size_t lds_bytes, hipStream_t stream);
 
 // Enqueue a zero fill of `bytes` (multiple of 4) at `p` (no hipMemsetAsync).
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream);
 
 // Templates instantiated for vecs_per_thread.
 bool supported_vecs_per_thread(int nv);
+
+// Dynamic LDS of a workgroup of `waves` pieces whose per-batch selection
+// needs sort_bytes.
+size_t group_lds_bytes(int waves, size_t sort_bytes);
 
 } // namespace rtopk

@@ -1,4 +1,4 @@
-// gfx950 (CDNA4) kernels of the hierarchical beam-search selection step.
+// gfx950 (CDNA4) kernel of the hierarchical beam-search selection step.
 //
 // The method is the LightSeq inference article's hierarchical decoding
 // (its passage on the logit rough-select kernel and the candidate queue):
@@ -6,39 +6,49 @@
 //          maximum and the minimum of those maxima -- the "R-top-k", never
 //          above the k-th largest logit -- and compute log_sum_exp in the
 //          same traversal;
-//  pass 2  keep every logit >= R-top-k in a device-memory candidate queue,
-//          written concurrently by many threads, one segment per batch
-//          element;
-//  sort    one small sort of each batch element's queue gives its exact top-k.
+//  pass 2  keep every logit >= R-top-k as a candidate of its batch element;
+//  sort    one small sort of each batch element's candidates gives its exact
+//          top-k.
 //
 // MI355X design (one launch per step, kernel `rtopk_step`):
-//  * A beam row is cut into `chunks` pieces; one 256-thread workgroup owns a
-//    piece and streams it once from HBM with 16-byte loads straight into
-//    registers (up to 12 x 16 B per thread), where it stays for both passes:
-//    HBM is read exactly once. Registers instead of LDS: the 512 KB VGPR file
-//    per CU holds more than the 160 KB LDS, and pass 2 compares straight from
-//    registers without an LDS round trip.
+//  * A beam row is cut into `chunks` contiguous pieces of 64 x NV 16-byte
+//    vectors. One wave64 owns a piece: every lane loads its NV vectors from
+//    HBM with 16-byte loads straight into registers, where they stay for both
+//    passes, so HBM is read exactly once. Pieces are independent: a wave
+//    never waits for another wave after its loads are issued, and the only
+//    cross-lane traffic is DPP, readlane and ballots inside the wave. A
+//    workgroup holds `waves` consecutive pieces: 16 when the whole grid is
+//    resident at once, 4 when workgroups run in rounds (a workgroup frees its
+//    CU only when its slowest wave is done).
 //  * Pass 1 keeps one running maximum per element slot (packed v_pk_max_f16
-//    for fp16), which yields the group maxima, with groups = element index
-//    mod ngroups; the log-sum-exp is accumulated online in fp32 in base 2,
-//    rescaled once per block of 4 vectors, with v_fma_mix/v_exp_f32.
-//  * Groups are combined by wave butterflies and LDS; the piece threshold is
-//    the k-th largest of the ngroups (k rounded up to a power of two) group
-//    maxima, i.e. the R-top-k itself when k is a power of two.
-//  * Pass 2 skips every thread whose maximum is below the threshold; hits are
-//    appended to an LDS stage with a wave ballot, mbcnt prefix and one LDS
-//    atomic per wave, then reserved in the batch element's global queue with
-//    one atomic per workgroup. A piece with more than `chunk_limit` hits
-//    emits only its own exact top-k (k rounds of block argmax), which keeps
-//    the result exact: a beam's top-k within any piece is inside that
-//    piece's own top-k.
-//  * The last workgroup of a batch element (device-scope ticket) merges the
-//    per-piece (max, sum) pairs in piece order, applies the tighter per-beam
-//    threshold max_c T_c and the batch bound S = max_j (alive_j + T_j -
-//    lse_j) (at least k candidates score >= S), and sorts the survivors with
-//    an LDS bitonic network on 64-bit keys (score desc, flat index asc).
-//    It then puts its ticket back to zero; tickets live in a region of the
-//    workspace that no shape uses for anything else.
+//    for fp16) and accumulates the log-sum-exp online in fp32, base 2,
+//    rescaled once per block of 4 vectors so that the work follows the
+//    arriving data. Group g holds the elements e = g mod ngroups, so a slot's
+//    maximum is a group maximum of the lane; DPP row reductions plus
+//    readlanes make the piece's group maxima. Its threshold is the k-th
+//    largest of the ngroups (k rounded up to a power of two) group maxima:
+//    the R-top-k itself when k is a power of two.
+//  * A piece may treat its own threshold as the row's: any logit among the
+//    row's top-k that lies in the piece is among the piece's top-k, and those
+//    are all >= the piece's threshold. So each piece publishes just its own
+//    exact top-k (by logit desc, flat index asc) among its logits >= T.
+//  * Pass 2 tests each vector with one packed maximum; a vector where some
+//    lane has a hit is examined element by element, hits are ranked by ballot
+//    + mbcnt into 64 LDS entries (one per lane) and the piece's top-k is found
+//    by rank counting (k rounds of wave argmax if more than `chunk_limit`).
+//  * Cross-workgroup data moves only through device-coherent (sc1) atomic
+//    stores and loads, so no L2 writeback or invalidate is ever needed.
+//    Device-scope atomics on one address serialise at the memory side, so
+//    arrivals are counted in two levels: the waves of a workgroup count
+//    themselves in LDS, and the last of them adds the workgroup's piece count
+//    to the ticket of each batch element it touched (two arrivals per ticket
+//    for 4 x 40000-logit batch elements). The wave that completes a ticket
+//    merges the pieces' (max, sum) partials by a fixed tree, applies the
+//    per-beam threshold max_c T_c and the batch bound
+//    S = max_j (alive_j + T_j - lse_j) (at least k candidates score >= S),
+//    and selects the k best survivors. It then puts the ticket back to zero;
+//    tickets live in a region of the workspace that no shape uses for
+//    anything else.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -51,8 +61,12 @@
 namespace rtopk {
 namespace {
 
-constexpr int kWaves = kThreads / 64;
 constexpr int kBlock = 4; // vectors per online log-sum-exp rescale
+// LDS of a workgroup: arrival counter, the shared group maxima of each of its
+// (at most `waves`) rows as order-preserving bits, then the waves' selection
+// LDS or, for the wave that completes a ticket, the sorter's.
+constexpr int kLdsShare = 256; // GroupLds (counters, reduction scratch) first
+__host__ __device__ constexpr size_t lds_header(int waves) { return kLdsShare + 4 * (size_t)waves * kMaxK; }
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.69314718055994530942f;
 
@@ -93,11 +107,15 @@ __device__ __forceinline__ uint64_t score_key(float score, uint32_t flat)
     return ((uint64_t)ord_bits(score + 0.0f) << 32) | (uint64_t)(0xffffffffu - flat);
 }
 
+// A published candidate is its sort key by logit, score_key(x, flat).
+__device__ __forceinline__ float entry_x(uint64_t e) { return from_ord((uint32_t)(e >> 32)); }
+__device__ __forceinline__ uint32_t entry_flat(uint64_t e) { return 0xffffffffu - (uint32_t)e; }
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 // Merge of two base-2 log-sum-exp partials (m = max in log2 units, s = sum of
-// 2^(x - m)). Symmetric in its arguments, so butterfly lanes agree bit for bit.
+// 2^(x - m)).
 __device__ __forceinline__ void lse_merge(float &m, float &s, float m2, float s2)
 {
     float M = fmaxf(m, m2);
@@ -110,12 +128,12 @@ __device__ __forceinline__ void lse_merge(float &m, float &s, float m2, float s2
     m = M;
 }
 
-// Cross-workgroup data (queue entries, partials, counters) moves only through
+// Cross-workgroup data (candidates, partials, counters) moves only through
 // agent-scope atomic stores and loads, which gfx950 issues with sc1: they are
 // performed at the device coherence point, past the per-XCD L2s, so no L2
 // writeback (buffer_wbl2) or invalidate (buffer_inv) is ever needed. A writer
-// drains its own stores (s_waitcnt vmcnt(0)) before its workgroup takes the
-// ticket; the compiler barriers keep the stores on their side of the wait.
+// drains its own stores (s_waitcnt vmcnt(0)) before it takes its ticket; the
+// compiler barriers keep the stores on their side of the wait.
 __device__ __forceinline__ void put64(uint64_t *p, uint64_t v)
 {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -128,26 +146,125 @@ __device__ __forceinline__ void put32(uint32_t *p, uint32_t v)
 {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint32_t get32(const uint32_t *p)
-{
-    return __hip_atomic_load(const_cast<uint32_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ __forceinline__ void drain_stores()
 {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0); // vmcnt(0) expcnt(0) lgkmcnt(0)
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int d)
-{
-    uint32_t lo = __shfl_xor((uint32_t)v, d);
-    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), d);
-    return ((uint64_t)hi << 32) | lo;
-}
 
+// q / d for 0 <= q < 2^22 and 1 <= d < 2^22, via one float multiply: the
+// quotient's error is below 1/(2d) of a unit, so (q + 0.5) * (1/d) never
+// crosses an integer boundary before the truncation.
+__device__ __forceinline__ int small_div(int q, float inv_d) { return (int)(((float)q + 0.5f) * inv_d); }
+
+// ---------------------------------------------------------------- wave primitives
+__device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+
+// Number of set bits of `mask` below this lane.
 __device__ __forceinline__ uint32_t lane_prefix(uint64_t mask)
 {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Wave-wide reductions with DPP row operations (VALU only, no LDS): swap
+// neighbours (quad_perm 1,0,3,2), swap pairs (quad_perm 2,3,0,1), mirror
+// within 8 lanes, mirror within 16 lanes -- after which every lane of a
+// 16-lane row holds the row's total -- then the four row totals are combined
+// in a fixed order from readlanes. Each step combines the same two values on
+// both partner lanes, so the result is identical on every lane and from run
+// to run. Every lane must be active.
+template <int CTRL> __device__ __forceinline__ float dpp_f(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float lane_f(float v, int lane)
+{
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+__device__ __forceinline__ float wave_max_f(float v)
+{
+    v = fmaxf(v, dpp_f<0xb1>(v));
+    v = fmaxf(v, dpp_f<0x4e>(v));
+    v = fmaxf(v, dpp_f<0x141>(v));
+    v = fmaxf(v, dpp_f<0x140>(v));
+    return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+}
+__device__ __forceinline__ float row16_max_f(float v) // every lane: the maximum over its 16-lane row
+{
+    v = fmaxf(v, dpp_f<0xb1>(v));
+    v = fmaxf(v, dpp_f<0x4e>(v));
+    v = fmaxf(v, dpp_f<0x141>(v));
+    return fmaxf(v, dpp_f<0x140>(v));
+}
+__device__ __forceinline__ float wave_min_f(float v)
+{
+    v = fminf(v, dpp_f<0xb1>(v));
+    v = fminf(v, dpp_f<0x4e>(v));
+    v = fminf(v, dpp_f<0x141>(v));
+    v = fminf(v, dpp_f<0x140>(v));
+    return fminf(fminf(lane_f(v, 0), lane_f(v, 16)), fminf(lane_f(v, 32), lane_f(v, 48)));
+}
+__device__ __forceinline__ float wave_sum_f(float v)
+{
+    v = v + dpp_f<0xb1>(v);
+    v = v + dpp_f<0x4e>(v);
+    v = v + dpp_f<0x141>(v);
+    v = v + dpp_f<0x140>(v);
+    return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
+{
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+        const uint32_t lo = __shfl_xor((uint32_t)v, d);
+        const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), d);
+        const uint64_t o = ((uint64_t)hi << 32) | lo;
+        v = o > v ? o : v;
+    }
+    return v;
+}
+__device__ __forceinline__ uint32_t first_u32(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v)
+{
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1)
+        v += __shfl_xor(v, d);
+    return v;
+}
+// Sum of v over the lanes below this one.
+__device__ __forceinline__ uint32_t wave_excl_scan_u32(uint32_t v, int lane)
+{
+    uint32_t x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t t = __shfl_up(x, d);
+        x += lane >= d ? t : 0u;
+    }
+    return x - v;
+}
+
+// Workgroup barrier that waits only for this wave's LDS (and scalar)
+// operations, s_waitcnt lgkmcnt(0) with vmcnt and expcnt at their maxima:
+// __syncthreads would also wait for every global load and store in flight,
+// and here barriers only ever order LDS accesses.
+__device__ __forceinline__ void lds_barrier()
+{
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Orders one wave's LDS accesses across its lanes (the wave runs in lockstep
+// and LDS executes its instructions in order, so compiler fences suffice).
+// Sibling waves are not waited for: code that only one wave runs uses this
+// instead of a workgroup barrier.
+__device__ __forceinline__ void wave_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // ------------------------------------------------------------- dtype traits
@@ -185,9 +302,9 @@ template <> struct Traits<0> { // float32
         for (int i = 0; i < 4; ++i)
             s[i] = a.v[i];
     }
-    __device__ static float vmax(const uint4 &d)
+    __device__ static bool any_ge(const uint4 &d, float T)
     {
-        return fmaxf(fmaxf(elem(d, 0), elem(d, 1)), fmaxf(elem(d, 2), elem(d, 3)));
+        return fmaxf(fmaxf(elem(d, 0), elem(d, 1)), fmaxf(elem(d, 2), elem(d, 3))) >= T;
     }
 };
 
@@ -244,11 +361,13 @@ template <> struct Traits<1> { // float16, max kept on packed pairs
             s[2 * p + 1] = (float)a.h[p].y;
         }
     }
-    __device__ static float vmax(const uint4 &d)
+    // T is an fp16 value widened (or -inf), so the comparison can stay in fp16
+    __device__ static bool any_ge(const uint4 &d, float T)
     {
         half2v t = __builtin_elementwise_max(__builtin_elementwise_max(pair(d, 0), pair(d, 1)),
                                              __builtin_elementwise_max(pair(d, 2), pair(d, 3)));
-        return fmaxf((float)t.x, (float)t.y);
+        const _Float16 th = (_Float16)T;
+        return t.x >= th || t.y >= th;
     }
 };
 
@@ -301,131 +420,21 @@ template <> struct Traits<2> { // bfloat16: widened to fp32 by a shift or a mask
         for (int i = 0; i < 8; ++i)
             s[i] = a.v[i];
     }
-    __device__ static float vmax(const uint4 &d)
+    __device__ static bool any_ge(const uint4 &d, float T)
     {
         float m = elem(d, 0);
 #pragma unroll
         for (int i = 1; i < 8; ++i)
             m = fmaxf(m, elem(d, i));
-        return m;
+        return m >= T;
     }
 };
-
-// ---------------------------------------------------------------- shared memory
-struct SelectSmem {
-    float gslot[kWaves][64]; // per-wave group maxima
-    float gm[64];            // group maxima of the piece
-    float wm[kWaves], ws[kWaves];
-    uint64_t stage[kMaxChunkLimit];
-    uint64_t kred[kWaves];
-    uint32_t nc;
-    float T;
-};
-
-struct SortSmem {
-    uint64_t keys[kSortKeys]; // survivors' sort keys
-    uint16_t pn[kMaxPieces];  // candidates per piece
-    float lse[kMaxBeam], thr[kMaxBeam], alive[kMaxBeam];
-    float fred[kWaves];
-    uint64_t kred[kWaves];
-    uint32_t ns, ndbg;
-};
-
-union Smem {
-    SelectSmem s;
-    SortSmem t;
-};
-
-// Wave-wide reductions with DPP row operations (VALU only, no LDS): swap
-// neighbours (quad_perm 1,0,3,2), swap pairs (quad_perm 2,3,0,1), mirror
-// within 8 lanes, mirror within 16 lanes -- after which every lane of a
-// 16-lane row holds the row's total -- then the four row totals are combined
-// in a fixed order from readlanes. Each step combines the same two values on
-// both partner lanes, so the result is identical on every lane and from run
-// to run.
-template <int CTRL> __device__ __forceinline__ float dpp_f(float v)
-{
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
-}
-__device__ __forceinline__ float lane_f(float v, int lane)
-{
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
-}
-__device__ __forceinline__ float wave_max_f(float v)
-{
-    v = fmaxf(v, dpp_f<0xb1>(v));
-    v = fmaxf(v, dpp_f<0x4e>(v));
-    v = fmaxf(v, dpp_f<0x141>(v));
-    v = fmaxf(v, dpp_f<0x140>(v));
-    return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
-}
-__device__ __forceinline__ float wave_sum_f(float v)
-{
-    v = v + dpp_f<0xb1>(v);
-    v = v + dpp_f<0x4e>(v);
-    v = v + dpp_f<0x141>(v);
-    v = v + dpp_f<0x140>(v);
-    return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
-}
-
-__device__ __forceinline__ float block_max_f(float v, float *red, int tid)
-{
-    v = wave_max_f(v);
-    if ((tid & 63) == 0)
-        red[tid >> 6] = v;
-    __syncthreads();
-    float r = red[0];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w)
-        r = fmaxf(r, red[w]);
-    __syncthreads();
-    return r;
-}
-
-__device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t *red, int tid)
-{
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-        uint64_t o = shfl_xor_u64(v, d);
-        v = o > v ? o : v;
-    }
-    if ((tid & 63) == 0)
-        red[tid >> 6] = v;
-    __syncthreads();
-    uint64_t r = red[0];
-#pragma unroll
-    for (int w = 1; w < kWaves; ++w)
-        r = red[w] > r ? red[w] : r;
-    __syncthreads();
-    return r;
-}
-
-// Descending bitonic sort of keys[0..P), P a power of two, whole workgroup.
-__device__ void bitonic_desc(uint64_t *keys, int P, int tid)
-{
-    for (int size = 2; size <= P; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = tid; i < (P >> 1); i += kThreads) {
-                int lo = 2 * i - (i & (stride - 1));
-                int hi = lo + stride;
-                bool desc = (lo & size) == 0;
-                uint64_t x = keys[lo], y = keys[hi];
-                if ((x < y) == desc) {
-                    keys[lo] = y;
-                    keys[hi] = x;
-                }
-            }
-            __syncthreads();
-        }
-    }
-}
-
-// A candidate slot holds the candidate's sort key by logit, score_key(x, flat):
-// the order-preserving bits of the logit above 0xffffffff - flat.
-__device__ __forceinline__ float entry_x(uint64_t e) { return from_ord((uint32_t)(e >> 32)); }
-__device__ __forceinline__ uint32_t entry_flat(uint64_t e) { return 0xffffffffu - (uint32_t)e; }
 
 // ------------------------------------------------------------ passes 1 and 2
+// Read in place of the finished mask when there is none (0), or in place of a
+// piece past the end of the grid (1), so that the flag load needs no branch.
+__device__ uint8_t kFlagConst[2] = {0, 1}; // global memory, like the mask: a global (not flat) load
+
 // Hides the staged vectors' values from the optimiser, so that pass 2
 // re-derives what it needs from the packed data instead of keeping every
 // converted element of pass 1 alive in registers.
@@ -439,38 +448,62 @@ __device__ __forceinline__ void opaque(uint4 &v)
 // with a neighbour row (kGeneral) are masked element by element.
 enum PieceMode { kAligned = 0, kGeneral = 1 };
 
+// LDS of the selection phase: the piece's candidates, one entry per lane.
+struct SelectLds {
+    uint64_t stage[kLanes];
+};
+static_assert(sizeof(SelectLds) % 16 == 0, "per-wave LDS regions stay 16-byte aligned");
+
 template <int DT, int NV, int MODE>
-__device__ void select_piece(const StepArgs &a, SelectSmem &sm, int row, int j, int c, int tid)
+__device__ __forceinline__ void select_piece(const StepArgs &a, SelectLds &sm, uint32_t *gshare_rows, long long u, bool valid,
+                             int lane)
 {
     using Tr = Traits<DT>;
     constexpr int EPV = Tr::epv;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int c = valid ? (int)(u % a.chunks) : 0;
+    const int row = valid ? (int)(u / a.chunks) : 0;
+    const int j = row % a.beam;
+    // this row's shared group maxima (rows are counted from the workgroup's first)
+    const long long row0 = (long long)(u - (u % a.waves)) / a.chunks;
+    uint32_t *gshare = gshare_rows + (row - row0) * kMaxK;
     // Vectors are counted in the 16-byte-aligned frame of the tensor; a row
     // starts `lead` elements into its first vector v0 and spans `span` vectors.
-    // Everything per thread is 32-bit and relative to the row.
+    // Everything per lane is 32-bit and relative to the row.
     const long long e0 = (long long)row * a.V + a.align_elems;
     const long long v0 = e0 / EPV;
     const int lead = (int)(e0 - v0 * EPV);
     const int span = (lead + a.V + EPV - 1) / EPV;
-    const int pbeg = c * a.vecs_per_chunk;                          // piece start, vectors from v0
+    const int pbeg = c * a.vecs_per_chunk; // piece start, vectors from v0
     const int pend = pbeg + a.vecs_per_chunk < span ? pbeg + a.vecs_per_chunk : span;
     const uint4 *src = reinterpret_cast<const uint4 *>(a.logits_aligned) + v0;
     const uint32_t flat0 = (uint32_t)j * (uint32_t)a.V - (uint32_t)lead; // flat index of slot 0 of vector 0
 
+    // The finished flag is loaded first but tested only once the piece's
+    // loads are in flight: its latency under a full memory system overlaps
+    // the stream instead of delaying it. The compiler fence keeps the loads
+    // on their side of the test (a finished row reads its piece for nothing).
+    const uint8_t *finp = !valid ? &kFlagConst[1] : a.finished != nullptr ? &a.finished[row] : &kFlagConst[0];
+    uint32_t fin = *finp;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     // Unconditional loads (index clamped into the piece) keep each load's
     // distance to its use visible to the waitcnt pass; empty or out-of-row
     // slots are overwritten with -inf at their use, by selects.
+    // (A wave past the last piece reads row 0's first piece and drops it: no
+    // branch around the loads, so the waitcnt pass counts them exactly.)
     uint4 d[NV];
     const int qlast = pend - 1;
 #pragma unroll
     for (int r = 0; r < NV; ++r) {
-        const int q = pbeg + tid + r * kThreads;
+        const int q = pbeg + lane + r * kLanes;
         d[r] = src[q < qlast ? q : qlast];
     }
-    // slots r < nfull hold valid vectors in every thread of the workgroup
-    const int nfull = pend > pbeg ? (pend - pbeg) / kThreads : 0;
+    asm volatile("" : "+v"(fin)); // the test waits for the flag here, past the loads
+    if (fin != 0)
+        return;
+    // slots r < nfull hold valid vectors in every lane
+    const int nfull = pend > pbeg ? (pend - pbeg) / kLanes : 0;
 
-    // ---- pass 1: group maxima + online log-sum-exp (base 2), one block of
+    // ---- pass 1: slot maxima + online log-sum-exp (base 2), one block of
     // kBlock vectors at a time so that the work follows the arriving data
     typename Tr::Acc acc;
     Tr::init(acc);
@@ -483,7 +516,7 @@ __device__ void select_piece(const StepArgs &a, SelectSmem &sm, int row, int j, 
         Tr::order_after(acc, s0, s1);
 #pragma unroll
         for (int r = r0; r < r0 + kBlock && r < NV; ++r) {
-            const int q = pbeg + tid + r * kThreads;
+            const int q = pbeg + lane + r * kLanes;
             if (MODE == kAligned) {
                 if (r >= nfull) { // uniform: never taken in a piece that fills its slots
                     const bool ok = q < pend;
@@ -517,15 +550,23 @@ __device__ void select_piece(const StepArgs &a, SelectSmem &sm, int row, int j, 
             }
         }
     }
-    float s = s0 + s1;
     const float tmax = Tr::amax(acc);
 
-    // ---- groups: fold slots to F = min(ngroups, EPV), reduce lanes that share groups
+    // ---- the piece's log-sum-exp partial: wave maximum, one rescale per lane, a sum
+    const float pm = wave_max_f(m2);
+    const float ps = wave_sum_f((pm == -INFINITY) ? 0.f : (s0 + s1) * fast_exp2(m2 - pm));
+
+    // ---- threshold. Slot i of a lane holds elements e = i mod EPV; folding
+    // slots i and i + h for h >= F = min(ngroups, EPV) leaves slot f with
+    // group f of this lane (ngroups <= EPV), or with group f of the lane's
+    // class lane mod D, D = ngroups / EPV (ngroups > EPV): pieces start on
+    // multiples of 64 vectors, so a vector's first element is lane mod D
+    // groups of EPV away from a multiple of ngroups.
     float slot[EPV];
     Tr::slots(acc, slot);
     const int ng = a.ngroups;
     const int F = ng < EPV ? ng : EPV;
-    const int D = ng / F; // lanes l and l' hold the same groups iff l = l' mod D
+    const int D = ng / F;
 #pragma unroll
     for (int h = EPV / 2; h >= 1; h >>= 1) {
         if (h >= F) {
@@ -534,311 +575,430 @@ __device__ void select_piece(const StepArgs &a, SelectSmem &sm, int row, int j, 
                 slot[i] = fmaxf(slot[i], slot[i + h]);
         }
     }
-    if (D == 1) { // every lane holds the same groups: plain wave maxima
+    // The R-top-k bound holds for any set of a row's logits: the k-th
+    // largest of its group maxima is at most its own k-th largest logit, so at
+    // most the row's. So the waves of a row share their group maxima in LDS
+    // (atomic max on order-preserving bits) and each takes the threshold of
+    // everything its row has published so far, itself included: the later
+    // waves of a row filter with nearly the whole row's R-top-k.
+    if (D == 1) {
 #pragma unroll
         for (int f = 0; f < EPV; ++f) {
             if (f < F) {
-                const float g = wave_max_f(slot[f]);
-                if (lane == 0)
-                    sm.gslot[wave][f] = g;
+                const float v = row16_max_f(slot[f]); // each 16-lane row's maximum
+                if ((lane & 15) == 0)
+                    atomicMax(&gshare[f], ord_bits(v));
             }
-        }
-    } else { // lanes l and l' share groups iff l = l' mod D: butterflies over distances >= D
-#pragma unroll
-        for (int f = 0; f < EPV; ++f) {
-            if (f < F) {
-                for (int dd = 32; dd >= D; dd >>= 1)
-                    slot[f] = fmaxf(slot[f], __shfl_xor(slot[f], dd));
-                if (lane < D)
-                    sm.gslot[wave][lane * F + f] = slot[f];
-            }
-        }
-    }
-    // wave log-sum-exp: the wave maximum first, then one rescale per lane and a sum
-    const float wm = wave_max_f(m2);
-    s = (wm == -INFINITY) ? 0.f : s * fast_exp2(m2 - wm);
-    s = wave_sum_f(s);
-    if (lane == 0) {
-        sm.wm[wave] = wm;
-        sm.ws[wave] = s;
-    }
-    if (tid == 0)
-        sm.nc = 0;
-    __syncthreads();
-    float pm = 0.f, ps = 0.f;
-    if (tid == 0) { // fixed merge order: waves 0..3
-        pm = sm.wm[0];
-        ps = sm.ws[0];
-        for (int w = 1; w < kWaves; ++w)
-            lse_merge(pm, ps, sm.wm[w], sm.ws[w]);
-    }
-    float T;
-    if (ng == a.k) {
-        // the R-top-k: minimum over the groups of the group maxima (each thread reads them all)
-        T = INFINITY;
-        for (int g = 0; g < ng; ++g) {
-            float v = sm.gslot[0][g];
-#pragma unroll
-            for (int w = 1; w < kWaves; ++w)
-                v = fmaxf(v, sm.gslot[w][g]);
-            T = fminf(T, v);
         }
     } else {
-        // k below a power of two: the k-th largest of the ngroups maxima
-        if (tid < ng) {
-            float g = sm.gslot[0][tid];
+        // lanes l and l' hold the same groups iff l = l' mod D: butterflies over
+        // distances >= D leave lane l < D with groups l*F .. l*F + F - 1
 #pragma unroll
-            for (int w = 1; w < kWaves; ++w)
-                g = fmaxf(g, sm.gslot[w][tid]);
-            sm.gm[tid] = g;
+        for (int f = 0; f < EPV; ++f) {
+            for (int dd = 32; dd >= D; dd >>= 1)
+                slot[f] = fmaxf(slot[f], __shfl_xor(slot[f], dd));
+            if (lane < D)
+                atomicMax(&gshare[lane * F + f], ord_bits(slot[f]));
         }
-        __syncthreads();
-        if (tid < ng) {
-            const float v = sm.gm[tid];
-            int gt = 0, ge = 0;
-            for (int u = 0; u < ng; ++u) {
-                const float w = sm.gm[u];
-                gt += w > v;
-                ge += w >= v;
-            }
-            if (gt < a.k && a.k <= ge)
-                sm.T = v;
+    }
+    wave_sync();
+    // One read per lane is the snapshot; each value is a group maximum over a
+    // subset of the row that contains this piece, which keeps the threshold
+    // below the row's k-th largest logit whatever the other waves do meanwhile.
+    const float cur = lane < ng ? from_ord(gshare[lane]) : INFINITY;
+    float T;
+    if (ng == a.k) { // the R-top-k: the least group maximum
+        T = wave_min_f(cur);
+    } else { // k below a power of two: the k-th largest of the ngroups maxima
+        int gt = 0, ge = 0;
+        for (int e = 0; e < ng; ++e) {
+            const float w = lane_f(cur, e);
+            gt += w > cur;
+            ge += w >= cur;
         }
-        __syncthreads();
-        T = sm.T;
+        T = wave_max_f(lane < ng && gt < a.k && a.k <= ge ? cur : -INFINITY);
     }
 
-    // ---- pass 2: stage the sort key of every valid logit >= T. A lane only
-    // examines the element positions (slots) whose running maximum reaches T
-    // -- usually none, rarely more than one -- across its vectors: it counts
-    // the hits, reserves them with one LDS atomic add (aggregated per wave by
-    // the compiler), and writes them.
-    if (tmax >= T) {
-        int qb0 = pbeg + tid; // opaque: keeps per-element index math inside this cold block
+    // ---- pass 2: stage the sort key of every valid logit >= T. The wave
+    // tests each of its vectors with one packed maximum; only a vector in
+    // which some lane holds a hit (a wave-uniform branch, usually taken once
+    // or twice per piece) is examined element by element. Hits are ranked by
+    // ballot + mbcnt, so the count is wave-uniform and no atomics are needed.
+    const uint32_t cap = (uint32_t)a.chunk_limit;
+    uint32_t wn = 0;
+    if (ballot(tmax >= T) != 0) {
+        int qb0 = pbeg + lane; // opaque: keeps per-element index math inside this block
         asm volatile("" : "+v"(qb0));
-        float sl[EPV];
-        Tr::slots(acc, sl);
-        auto hit = [&](int r, int i, float x) {
-            const int q = qb0 + r * kThreads;
-            const int t = q * EPV + i - lead;
-            return x >= T && q < pend && (MODE != kGeneral || (t >= 0 && t < a.V));
-        };
-        uint32_t cnt = 0;
 #pragma unroll
-        for (int i = 0; i < EPV; ++i) {
-            if (sl[i] >= T) {
+        for (int r = 0; r < NV; ++r) {
+            opaque(d[r]);
+            if (ballot(Tr::any_ge(d[r], T)) != 0) {
+                const int q = qb0 + r * kLanes;
+                const bool inq = q < pend;
 #pragma unroll
-                for (int r = 0; r < NV; ++r) {
-                    opaque(d[r]);
-                    cnt += hit(r, i, Tr::elem(d[r], i));
-                }
-            }
-        }
-        uint32_t pos = atomicAdd(&sm.nc, cnt);
-#pragma unroll
-        for (int i = 0; i < EPV; ++i) {
-            if (sl[i] >= T) {
-#pragma unroll
-                for (int r = 0; r < NV; ++r) {
-                    opaque(d[r]);
+                for (int i = 0; i < EPV; ++i) {
                     const float x = Tr::elem(d[r], i);
-                    if (hit(r, i, x)) {
-                        if (pos < (uint32_t)a.chunk_limit)
-                            sm.stage[pos] = score_key(x, flat0 + (uint32_t)((qb0 + r * kThreads) * EPV + i));
-                        ++pos;
+                    const int t = q * EPV + i - lead;
+                    const bool h = x >= T && inq && (MODE != kGeneral || (t >= 0 && t < a.V));
+                    const uint64_t m = ballot(h);
+                    if (m != 0) {
+                        const uint32_t pos = wn + lane_prefix(m);
+                        if (h && pos < cap)
+                            sm.stage[pos] = score_key(x, flat0 + (uint32_t)(q * EPV + i));
+                        wn += (uint32_t)__builtin_popcountll(m);
                     }
                 }
             }
         }
     }
-    __syncthreads();
-    const uint32_t nc = sm.nc;
-    const long long u = (long long)row * a.chunks + c;
-    uint64_t *mine = a.slots + u * a.k; // this piece's k candidate slots
-    uint32_t emit;
-    if (nc <= (uint32_t)a.chunk_limit) {
-        // The piece's own top-k by (logit desc, flat asc): only those can be
-        // among the batch element's top-k. Keys are distinct, so ranks are
-        // unique; slot r receives the key of rank r.
-        emit = nc < (uint32_t)a.k ? nc : (uint32_t)a.k;
-        if ((uint32_t)tid < nc) {
-            const uint64_t key = sm.stage[tid];
-            uint32_t rank = tid;
-            if (nc > (uint32_t)a.k) {
-                rank = 0;
-                for (uint32_t i = 0; i < nc; ++i)
-                    rank += sm.stage[i] > key;
-            }
-            if (rank < (uint32_t)a.k)
-                put64(&mine[rank], key);
-        }
-    } else {
-        // more candidates than the stage holds: k rounds of block argmax over the registers
-        emit = (uint32_t)a.k;
-        uint64_t prev = ~0ull;
-        for (int round = 0; round < a.k; ++round) {
-            uint64_t best = 0;
-            int qb0 = pbeg + tid; // opaque per round: no key hoisted out of the round loop
-            asm volatile("" : "+v"(qb0));
+    wave_sync();
+
+    // ---- more hits than the stage holds (heavy ties): find v, the piece's
+    // k-th largest logit counted with multiplicity, by walking its distinct
+    // values down from the top (one round when the top value repeats k
+    // times); then stage every logit > v and the first k - #(> v) logits == v
+    // in flat order (vectors, then lanes, then elements). That is exactly the
+    // piece's top-k by (logit desc, flat asc).
+    uint32_t nst = wn; // staged keys
+    if (wn > cap) {
+        int qb0 = pbeg + lane; // opaque: keeps per-element index math inside this block
+        asm volatile("" : "+v"(qb0));
+        auto valid = [&](int r, int i) {
+            const int q = qb0 + r * kLanes;
+            const int t = q * EPV + i - lead;
+            return q < pend && (MODE != kGeneral || (t >= 0 && t < a.V));
+        };
+        float prev = INFINITY, v = -INFINITY;
+        uint32_t above = 0;
+        for (int round = 0; round < a.k; ++round) { // wn > cap >= k valid logits are >= T
+            float mx = -INFINITY;
 #pragma unroll
             for (int r = 0; r < NV; ++r) {
-                const int q = qb0 + r * kThreads;
                 opaque(d[r]);
-                if (q < pend) {
-#pragma unroll 1
-                    for (int i = 0; i < EPV; ++i) {
-                        const int t = q * EPV + i - lead;
-                        if (MODE != kGeneral || (t >= 0 && t < a.V)) {
-                            const uint64_t key = score_key(Tr::elem_rt(d[r], i), flat0 + (uint32_t)(q * EPV + i));
-                            if (key < prev && key > best)
-                                best = key;
-                        }
-                    }
+#pragma unroll
+                for (int i = 0; i < EPV; ++i) {
+                    const float x = Tr::elem(d[r], i);
+                    mx = valid(r, i) && x < prev ? fmaxf(mx, x) : mx;
                 }
             }
-            best = block_max_u64(best, sm.kred, tid);
-            if (tid == 0)
-                put64(&mine[round], best);
-            prev = best;
+            v = wave_max_f(mx);
+            uint32_t c = 0;
+#pragma unroll
+            for (int r = 0; r < NV; ++r) {
+                opaque(d[r]);
+#pragma unroll
+                for (int i = 0; i < EPV; ++i)
+                    c += valid(r, i) && Tr::elem(d[r], i) == v;
+            }
+            c = wave_sum_u32(c);
+            if (above + c >= (uint32_t)a.k)
+                break;
+            above += c;
+            prev = v;
         }
+        nst = 0;
+#pragma unroll
+        for (int r = 0; r < NV; ++r) { // the logits > v
+            opaque(d[r]);
+            const int q = qb0 + r * kLanes;
+#pragma unroll
+            for (int i = 0; i < EPV; ++i) {
+                const float x = Tr::elem(d[r], i);
+                const bool h = valid(r, i) && x > v;
+                const uint64_t m = ballot(h);
+                if (m != 0) {
+                    if (h)
+                        sm.stage[nst + lane_prefix(m)] = score_key(x, flat0 + (uint32_t)(q * EPV + i));
+                    nst += (uint32_t)__builtin_popcountll(m);
+                }
+            }
+        }
+        uint32_t need = (uint32_t)a.k - above;
+#pragma unroll
+        for (int r = 0; r < NV; ++r) { // the first `need` logits == v
+            if (need == 0) // uniform; no break, so the loop unrolls and d[] stays in registers
+                continue;
+            opaque(d[r]);
+            const int q = qb0 + r * kLanes;
+            uint32_t bits = 0;
+#pragma unroll
+            for (int i = 0; i < EPV; ++i)
+                bits |= (uint32_t)(valid(r, i) && Tr::elem(d[r], i) == v) << i;
+            const uint32_t cnt = (uint32_t)__builtin_popcount(bits);
+            const uint32_t before = wave_excl_scan_u32(cnt, lane);
+            const uint32_t total = first_u32(__builtin_amdgcn_readlane(before + cnt, 63));
+#pragma unroll
+            for (int i = 0; i < EPV; ++i) {
+                const uint32_t rank = before + (uint32_t)__builtin_popcount(bits & ((1u << i) - 1u));
+                if (((bits >> i) & 1u) && rank < need)
+                    sm.stage[nst + rank] = score_key(Tr::elem(d[r], i), flat0 + (uint32_t)(q * EPV + i));
+            }
+            const uint32_t took = total < need ? total : need;
+            nst += took;
+            need -= took;
+        }
+        wave_sync();
     }
-    if (tid == 0) {
-        put64(&a.head[2 * u], ((uint64_t)__float_as_uint(ps) << 32) | __float_as_uint(pm));
-        put64(&a.head[2 * u + 1], ((uint64_t)emit << 32) | __float_as_uint(T));
+
+    // ---- publish this piece's own top-min(hits, k) by (logit desc, flat
+    // asc), in no particular slot order: only those can be among the batch
+    // element's top-k. Keys are distinct, so ranks are unique.
+    uint64_t *mine = a.slots + (long long)u * a.k;
+    const uint32_t emit = nst < (uint32_t)a.k ? nst : (uint32_t)a.k;
+    if ((uint32_t)lane < nst) {
+        const uint64_t key = sm.stage[lane];
+        uint32_t rank = lane;
+        if (nst > (uint32_t)a.k) {
+            rank = 0;
+#pragma unroll 8
+            for (uint32_t i = 0; i < nst; ++i)
+                rank += sm.stage[i] > key;
+        }
+        if (rank < (uint32_t)a.k)
+            put64(&mine[rank], key);
+    }
+    if (lane == 0) {
+        put64(&a.head[2 * (long long)u], ((uint64_t)__float_as_uint(ps) << 32) | __float_as_uint(pm));
+        put64(&a.head[2 * (long long)u + 1], ((uint64_t)emit << 32) | __float_as_uint(T));
         if (a.dbg_T)
             a.dbg_T[u] = T;
         if (a.dbg_hits)
-            a.dbg_hits[u] = nc;
+            a.dbg_hits[u] = wn;
     }
-    // every store of this workgroup is performed before it takes its ticket
-    // (the barrier that follows does not wait for memory)
+    // every store of this wave is performed before it takes its ticket
     drain_stores();
 }
 
 // ------------------------------------------------------------ per-batch selection
-// Run by the last workgroup of batch element b. One round trip loads every
-// piece header plus the first S slots of every piece; the beams' log-sum-exp
-// are merged in piece order; candidates are filtered by the per-beam
-// threshold and by the batch bound; the k best survivors are found by rank
-// counting (or a bitonic sort when there are many).
-__device__ void sort_batch(const StepArgs &a, SortSmem &sm, int b, int tid)
-{
-    const int beam = a.beam, C = a.chunks, L = a.k; // k slots per piece
-    const int P = beam * C;
-    const long long u0 = (long long)b * P;
-    // speculative slice: the first S slots of every piece p with (p+1)*S <= kSpec*kThreads
-    constexpr int kSpec = 4;
-    int S = kSpec * kThreads / P;
-    S = S < 1 ? 1 : (S > 32 ? 32 : S);
-    S = S < L ? S : L; // never past the piece's own slots
-    const int R = (P * S + kThreads - 1) / kThreads < kSpec ? (P * S + kThreads - 1) / kThreads : kSpec;
-    const bool has_fin = a.finished != nullptr;
+// LDS of the selection of batch element b, laid out by the host: sort keys,
+// per-piece partials, per-beam tables, per-piece candidate counts.
+struct SortLds {
+    uint64_t *keys;           // [sort_keys]
+    float *pm, *ps, *pt;      // [pieces] max2, sum, threshold of each piece
+    float *lse, *thr, *alive; // [beam]
+    uint8_t *pn;              // [pieces] candidates each piece published
+    uint8_t *fin;             // [beam] finished flags
+};
 
-    // ---- A: per-beam merge of the piece headers (fixed piece order) and the
-    // speculative slots; all of these loads are independent of each other
+// Counters and reduction scratch of a workgroup, in front of its LDS.
+struct GroupLds {
+    uint32_t todo[2]; // batch elements whose ticket this workgroup completed
+    uint32_t ns, ndbg;
+    float fred[kMaxWaves];
+    uint64_t kred[kMaxWaves];
+};
+
+static_assert(sizeof(GroupLds) <= kLdsShare, "GroupLds fits in front of the shared group maxima");
+
+__device__ __forceinline__ SortLds sort_lds(uint8_t *base, const StepArgs &a)
+{
+    const int P = a.beam * a.chunks;
+    SortLds sm;
+    sm.keys = reinterpret_cast<uint64_t *>(base);
+    sm.pm = reinterpret_cast<float *>(base + 8 * (size_t)a.sort_keys);
+    sm.ps = sm.pm + P;
+    sm.pt = sm.ps + P;
+    sm.lse = sm.pt + P;
+    sm.thr = sm.lse + a.beam;
+    sm.alive = sm.thr + a.beam;
+    sm.pn = reinterpret_cast<uint8_t *>(sm.alive + a.beam);
+    sm.fin = sm.pn + P;
+    return sm;
+}
+
+// Workgroup-wide maxima (every wave of the workgroup takes part).
+__device__ __forceinline__ float block_max_f(float v, GroupLds &g, int lane, int wave, int W)
+{
+    v = wave_max_f(v);
+    if (lane == 0)
+        g.fred[wave] = v;
+    lds_barrier();
+    float r = g.fred[0];
+    for (int w = 1; w < W; ++w)
+        r = fmaxf(r, g.fred[w]);
+    lds_barrier();
+    return r;
+}
+__device__ __forceinline__ uint64_t block_max_u64(uint64_t v, GroupLds &g, int lane, int wave, int W)
+{
+    v = wave_max_u64(v);
+    if (lane == 0)
+        g.kred[wave] = v;
+    lds_barrier();
+    uint64_t r = g.kred[0];
+    for (int w = 1; w < W; ++w)
+        r = g.kred[w] > r ? g.kred[w] : r;
+    lds_barrier();
+    return r;
+}
+
+// Descending bitonic sort of keys[0..P), P a power of two, whole workgroup.
+__device__ __forceinline__ void bitonic_desc(uint64_t *keys, int P, int tid, int nth)
+{
+    for (int size = 2; size <= P; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = tid; i < (P >> 1); i += nth) {
+                int lo = 2 * i - (i & (stride - 1));
+                int hi = lo + stride;
+                bool desc = (lo & size) == 0;
+                uint64_t x = keys[lo], y = keys[hi];
+                if ((x < y) == desc) {
+                    keys[lo] = y;
+                    keys[hi] = x;
+                }
+            }
+            lds_barrier();
+        }
+    }
+}
+
+// Run by the whole workgroup that completed the ticket of batch element b. One
+// round trip loads every piece header, the beams' flags and scores and the
+// first kSpec*threads published candidates; each beam's partials are merged
+// by a fixed binary tree over its pieces; candidates are filtered by the
+// per-beam threshold and the batch bound and ranked into LDS by ballot; the k
+// best survivors are found by rank counting (a bitonic sort when many).
+__device__ __forceinline__ void sort_batch(const StepArgs &a, const SortLds &sm, GroupLds &g, int b, int tid, int W)
+{
+    const int lane = tid & (kLanes - 1), wave = tid / kLanes, nth = W * kLanes;
+    const int beam = a.beam, C = a.chunks, L = a.k;
+    const int P = beam * C, NS = P * L; // pieces and published slots of b
+    const uint64_t *slots = a.slots + (long long)b * NS;
+    const uint64_t *head = a.head + 2 * (long long)b * P;
+    const uint32_t K = (uint32_t)a.sort_keys;
+    const bool has_fin = a.finished != nullptr;
+    const uint8_t *finb = has_fin ? a.finished + (long long)b * beam : nullptr;
+    const float invC = 1.f / (float)C, invL = 1.f / (float)L;
+
+    // ---- A: speculative slot loads, every header, the beams' flags and
+    // scores, all in flight at once. A finished beam published nothing this
+    // call: its stale partials are merged and ignored, its counts zeroed.
+    constexpr int kSpec = 4;
     uint64_t spec[kSpec];
 #pragma unroll
     for (int r = 0; r < kSpec; ++r) {
-        const int g = tid + r * kThreads;
-        spec[r] = 0ull;
-        if (r < R && g < P * S) {
-            const int p = g / S;
-            spec[r] = get64(&a.slots[(u0 + p) * L + (g - p * S)]);
-        }
+        const int gi = tid + r * nth;
+        spec[r] = gi < NS ? get64(&slots[gi]) : 0ull;
     }
     if (tid == 0) {
-        sm.ns = 0;
-        sm.ndbg = 0;
+        g.ns = 0;
+        g.ndbg = 0;
     }
-    float bound = -INFINITY;
-    for (int jj = tid; jj < beam; jj += kThreads) {
-        const bool fin = has_fin && a.finished[b * beam + jj];
-        const float alv = a.alive[b * beam + jj];
-        float lse = __uint_as_float(0x7fc00000u), thr = INFINITY; // NaN marks a finished beam
-        if (!fin) {
-            float M = -INFINITY, Ssum = 0.f, Tm = -INFINITY;
-            const uint64_t *h = a.head + 2 * (u0 + (long long)jj * C);
-            for (int c0 = 0; c0 < C; c0 += 8) { // headers of 8 pieces in flight at once
-                uint64_t hb[16];
+    for (int jj = tid; jj < beam; jj += nth) {
+        sm.alive[jj] = a.alive[b * beam + jj];
+        sm.fin[jj] = has_fin ? finb[jj] : 0;
+    }
+    for (int p0 = 0; p0 < P; p0 += 2 * nth) {
+        uint64_t hb[4];
+        uint32_t fb[2];
 #pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    hb[i] = c0 + (i >> 1) < C ? get64(&h[2 * c0 + i]) : 0ull;
+        for (int i = 0; i < 2; ++i) {
+            const int p = p0 + tid + i * nth;
+            hb[2 * i] = p < P ? get64(&head[2 * p]) : 0ull;
+            hb[2 * i + 1] = p < P ? get64(&head[2 * p + 1]) : 0ull;
+            fb[i] = p < P && has_fin ? finb[small_div(p, invC)] : 0u;
+        }
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    if (c0 + i < C) {
-                        lse_merge(M, Ssum, __uint_as_float((uint32_t)hb[2 * i]),
-                                  __uint_as_float((uint32_t)(hb[2 * i] >> 32)));
-                        Tm = fmaxf(Tm, __uint_as_float((uint32_t)hb[2 * i + 1]));
-                        sm.pn[jj * C + c0 + i] = (uint16_t)(hb[2 * i + 1] >> 32);
-                    }
-                }
+        for (int i = 0; i < 2; ++i) {
+            const int p = p0 + tid + i * nth;
+            if (p < P) {
+                sm.pm[p] = __uint_as_float((uint32_t)hb[2 * i]);
+                sm.ps[p] = __uint_as_float((uint32_t)(hb[2 * i] >> 32));
+                sm.pt[p] = __uint_as_float((uint32_t)hb[2 * i + 1]);
+                sm.pn[p] = fb[i] ? 0 : (uint8_t)(hb[2 * i + 1] >> 32);
             }
-            lse = (M + fast_log2(Ssum)) * kLn2;
-            thr = Tm;
+        }
+    }
+    // each beam's pieces merged pairwise at doubling distances: a fixed tree,
+    // so the result does not depend on arrival order
+    for (int stride = 1; stride < C; stride <<= 1) {
+        lds_barrier();
+        for (int p = tid; p < P; p += nth) {
+            const int c = p - small_div(p, invC) * C;
+            if ((c & (2 * stride - 1)) == 0 && c + stride < C) {
+                float m = sm.pm[p], sum = sm.ps[p];
+                lse_merge(m, sum, sm.pm[p + stride], sm.ps[p + stride]);
+                sm.pm[p] = m;
+                sm.ps[p] = sum;
+                sm.pt[p] = fmaxf(sm.pt[p], sm.pt[p + stride]);
+            }
+        }
+    }
+    lds_barrier();
+    float bound = -INFINITY;
+    for (int jj = tid; jj < beam; jj += nth) {
+        const float alv = sm.alive[jj];
+        float lse = __uint_as_float(0x7fc00000u), thr = INFINITY; // NaN marks a finished beam
+        if (!sm.fin[jj]) {
+            lse = (sm.pm[jj * C] + fast_log2(sm.ps[jj * C])) * kLn2;
+            thr = sm.pt[jj * C];
             // at least k logits of this beam are >= thr, so at least k
             // candidates score >= alive + (thr - lse)
             bound = fmaxf(bound, alv + (thr - lse));
-        } else {
-            for (int cc = 0; cc < C; ++cc)
-                sm.pn[jj * C + cc] = 0;
         }
         sm.lse[jj] = lse;
         sm.thr[jj] = thr;
-        sm.alive[jj] = alv;
         if (a.dbg_lse)
             a.dbg_lse[b * beam + jj] = lse;
     }
-    bound = block_max_f(bound, sm.fred, tid); // its barriers also publish the tables above
+    bound = block_max_f(bound, g, lane, wave, W); // its barriers also publish the tables
 
-    // ---- B: survivors -> sort keys, from the speculative slice and from the
-    // slots past it (loaded here, pieces handled one per thread)
-    auto consider = [&](uint64_t ent, int jj) {
-        const float x = entry_x(ent);
-        if (x >= sm.thr[jj]) {
-            const float sc = sm.alive[jj] + (x - sm.lse[jj]);
-            if (sc >= bound) {
-                const uint32_t pos = atomicAdd(&sm.ns, 1u);
-                if (pos < (uint32_t)kSortKeys)
-                    sm.keys[pos] = score_key(sc, entry_flat(ent));
-            }
+    // ---- B: survivors -> sort keys, ranked into LDS by ballot, one LDS atomic per wave
+    auto offer = [&](bool ok, uint64_t key) {
+        const uint64_t m = ballot(ok);
+        if (m != 0) {
+            uint32_t base = 0;
+            if (lane == 0)
+                base = atomicAdd(&g.ns, (uint32_t)__builtin_popcountll(m));
+            const uint32_t pos = first_u32(base) + lane_prefix(m);
+            if (ok && pos < K)
+                sm.keys[pos] = key;
         }
+    };
+    auto survivor = [&](int gi, uint64_t ent, uint64_t &key) {
+        const int p = small_div(gi, invL);
+        if (gi - p * L >= (int)sm.pn[p]) // slots past a piece's count hold stale data
+            return false;
+        const int jj = small_div(p, invC);
+        const float x = entry_x(ent);
+        if (!(x >= sm.thr[jj]))
+            return false;
+        const float sc = sm.alive[jj] + (x - sm.lse[jj]);
+        key = score_key(sc, entry_flat(ent));
+        return sc >= bound;
     };
 #pragma unroll
     for (int r = 0; r < kSpec; ++r) {
-        const int g = tid + r * kThreads;
-        if (r < R && g < P * S) {
-            const int p = g / S;
-            if (g - p * S < (int)sm.pn[p]) // slots past a piece's count hold stale data
-                consider(spec[r], p / C);
-        }
+        const int gi = tid + r * nth;
+        uint64_t key = 0;
+        const bool ok = gi < NS && survivor(gi, spec[r], key);
+        offer(ok, key);
     }
-    const int covered = R * kThreads / S; // pieces whose first S slots were loaded above
-    for (int p = tid; p < P; p += kThreads) {
-        const int n = (int)sm.pn[p];
-        const int jj = p / C;
-        for (int e0 = p < covered ? S : 0; e0 < n; e0 += 8) { // 8 loads in flight
-            uint64_t eb[8];
+    for (int g0 = kSpec * nth; g0 < NS; g0 += 4 * nth) { // 4 loads per thread in flight
+        uint64_t eb[4];
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                eb[i] = e0 + i < n ? get64(&a.slots[(u0 + p) * L + e0 + i]) : 0ull;
+        for (int i = 0; i < 4; ++i) {
+            const int gi = g0 + tid + i * nth;
+            eb[i] = gi < NS ? get64(&slots[gi]) : 0ull;
+        }
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                if (e0 + i < n)
-                    consider(eb[i], jj);
+        for (int i = 0; i < 4; ++i) {
+            const int gi = g0 + tid + i * nth;
+            uint64_t key = 0;
+            const bool ok = gi < NS && survivor(gi, eb[i], key);
+            offer(ok, key);
         }
     }
     if (has_fin) {
-        for (int jj = tid; jj < beam; jj += kThreads) {
-            if (a.finished[b * beam + jj] && sm.alive[jj] >= bound) {
-                const uint32_t pos = atomicAdd(&sm.ns, 1u);
-                if (pos < (uint32_t)kSortKeys)
-                    sm.keys[pos] =
-                        score_key(sm.alive[jj], (uint32_t)jj * (uint32_t)a.V + (uint32_t)a.eos_id);
-            }
+        for (int j0 = 0; j0 < beam; j0 += nth) {
+            const int jj = j0 + tid;
+            const bool ok = jj < beam && sm.fin[jj] && sm.alive[jj] >= bound;
+            const uint64_t key = ok ? score_key(sm.alive[jj], (uint32_t)jj * (uint32_t)a.V + (uint32_t)a.eos_id) : 0ull;
+            offer(ok, key);
         }
     }
-    __syncthreads();
-    const uint32_t ns = sm.ns;
+    lds_barrier();
+    const uint32_t ns = g.ns;
 
     // ---- D: the k best keys, in order
     auto emit_out = [&](int p, uint64_t key) {
@@ -849,48 +1009,40 @@ __device__ void sort_batch(const StepArgs &a, SortSmem &sm, int b, int tid)
         a.out_token[o] = (int32_t)(flat - jj * (uint32_t)a.V);
         a.out_score[o] = from_ord((uint32_t)(key >> 32));
     };
-    if (ns <= (uint32_t)kThreads) {
+    if (ns <= (uint32_t)nth) {
         // rank counting: keys are distinct (flat indices are), so ranks are a permutation
         if ((uint32_t)tid < ns) {
             const uint64_t mine = sm.keys[tid];
             uint32_t rank = 0;
+#pragma unroll 8
             for (uint32_t i = 0; i < ns; ++i)
                 rank += sm.keys[i] > mine;
             if (rank < (uint32_t)a.k)
                 emit_out((int)rank, mine);
         }
-    } else if (ns <= (uint32_t)kSortKeys) {
+    } else if (ns <= K) {
         int Pw = 2;
         while ((uint32_t)Pw < ns)
             Pw <<= 1;
-        for (int i = (int)ns + tid; i < Pw; i += kThreads)
+        for (int i = (int)ns + tid; i < Pw; i += nth)
             sm.keys[i] = 0ull; // below every real key
-        __syncthreads();
-        bitonic_desc(sm.keys, Pw, tid);
-        for (int p = tid; p < a.k && (uint32_t)p < ns; p += kThreads)
+        lds_barrier();
+        bitonic_desc(sm.keys, Pw, tid, nth);
+        for (int p = tid; p < a.k && (uint32_t)p < ns; p += nth)
             emit_out(p, sm.keys[p]);
     } else {
-        // more survivors than the LDS holds: k rounds of block argmax over every entry
+        // more survivors than the LDS holds: k rounds of workgroup argmax over every candidate
         uint64_t prev = ~0ull;
         for (int round = 0; round < a.k; ++round) {
             uint64_t best = 0;
-            for (int p = tid; p < P; p += kThreads) {
-                const int jj = p / C;
-                const int n = (int)sm.pn[p];
-                for (int e = 0; e < n; ++e) {
-                    const uint64_t ent = get64(&a.slots[(u0 + p) * L + e]);
-                    const float x = entry_x(ent);
-                    if (x >= sm.thr[jj]) {
-                        const float sc = sm.alive[jj] + (x - sm.lse[jj]);
-                        const uint64_t key = score_key(sc, entry_flat(ent));
-                        if (sc >= bound && key < prev && key > best)
-                            best = key;
-                    }
-                }
+            for (int gi = tid; gi < NS; gi += nth) {
+                uint64_t key = 0;
+                if (survivor(gi, get64(&slots[gi]), key) && key < prev && key > best)
+                    best = key;
             }
             if (has_fin) {
-                for (int jj = tid; jj < beam; jj += kThreads) {
-                    if (a.finished[b * beam + jj] && sm.alive[jj] >= bound) {
+                for (int jj = tid; jj < beam; jj += nth) {
+                    if (sm.fin[jj] && sm.alive[jj] >= bound) {
                         const uint64_t key =
                             score_key(sm.alive[jj], (uint32_t)jj * (uint32_t)a.V + (uint32_t)a.eos_id);
                         if (key < prev && key > best)
@@ -898,14 +1050,14 @@ __device__ void sort_batch(const StepArgs &a, SortSmem &sm, int b, int tid)
                     }
                 }
             }
-            best = block_max_u64(best, sm.kred, tid);
+            best = block_max_u64(best, g, lane, wave, W);
             prev = best;
             if (tid == 0 && best != 0ull)
                 emit_out(round, best);
         }
     }
     // padding when fewer than k candidates exist at all
-    for (int p = (int)ns + tid; p < a.k; p += kThreads) {
+    for (int p = (int)ns + tid; p < a.k; p += nth) {
         const long long o = (long long)b * a.k + p;
         a.out_beam[o] = -1;
         a.out_token[o] = -1;
@@ -914,52 +1066,88 @@ __device__ void sort_batch(const StepArgs &a, SortSmem &sm, int b, int tid)
 
     // ---- E: debug copies; the ticket goes back to zero for the next call. Headers
     // and slots need no clearing: every piece of an alive beam rewrites its
-    // header before taking its ticket, and slots are read only below a count.
+    // header before its arrival is counted, and slots are read only below a count.
     if (a.dbg_queue || a.dbg_count) {
-        __syncthreads();
+        lds_barrier();
         uint64_t *dq = a.dbg_queue ? a.dbg_queue + (long long)b * a.queue_cap : nullptr;
-        for (int p = tid; p < P; p += kThreads) {
+        for (int p = tid; p < P; p += nth) {
             const int n = (int)sm.pn[p];
-            const uint32_t base = atomicAdd(&sm.ndbg, (uint32_t)n);
+            const uint32_t base = atomicAdd(&g.ndbg, (uint32_t)n);
             if (dq)
                 for (int e = 0; e < n; ++e) {
-                    const uint64_t ent = get64(&a.slots[(u0 + p) * L + e]);
+                    const uint64_t ent = get64(&slots[(long long)p * L + e]);
                     dq[base + e] = ((uint64_t)__float_as_uint(entry_x(ent)) << 32) | entry_flat(ent);
                 }
         }
-        __syncthreads();
+        lds_barrier();
         if (tid == 0 && a.dbg_count)
-            a.dbg_count[b] = sm.ndbg;
+            a.dbg_count[b] = g.ndbg;
     }
     if (tid == 0)
         put32(&a.ticket[b], 0u);
 }
 
 template <int DT, int NV, bool ALIGNED>
-__global__ __launch_bounds__(kThreads) void rtopk_step(const StepArgs a)
+__global__ __launch_bounds__(kLanes *kMaxWaves) void rtopk_step(const StepArgs a)
 {
-    __shared__ Smem sm;
-    __shared__ uint32_t is_last;
-    const int tid = threadIdx.x;
-    const int u = blockIdx.x;
-    const int c = u % a.chunks;
-    const int row = u / a.chunks;
-    const int b = row / a.beam;
-    const int j = row - b * a.beam;
-    const bool fin = a.finished && a.finished[row];
-    if (!fin)
-        select_piece<DT, NV, ALIGNED ? kAligned : kGeneral>(a, sm.s, row, j, c, tid);
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t old =
-            __hip_atomic_fetch_add(&a.ticket[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        is_last = old == (uint32_t)(a.beam * a.chunks - 1); // every piece of b has published
+    extern __shared__ __align__(16) uint8_t lds[];
+    GroupLds &g = *reinterpret_cast<GroupLds *>(lds);
+    const int tid = threadIdx.x, lane = tid & (kLanes - 1), wave = tid / kLanes;
+    const int W = a.waves;
+    const size_t hdr = lds_header(W);
+    const long long total = (long long)a.B * a.beam * a.chunks; // pieces
+    const long long ufirst = (long long)blockIdx.x * W;
+    const long long u = ufirst + wave;
+    uint32_t *gshare = reinterpret_cast<uint32_t *>(lds + kLdsShare);
+    // The barrier before the loads orders the clearing of the shared group
+    // maxima before any wave's use; after the loads it would hold every wave
+    // until the last of the workgroup's loads could issue.
+    for (int i = tid; i < W * kMaxK; i += kLanes * W)
+        gshare[i] = 0x007fffffu; // ord_bits(-inf)
+    lds_barrier();
+    select_piece<DT, NV, ALIGNED ? kAligned : kGeneral>(
+        a, *reinterpret_cast<SelectLds *>(lds + hdr + wave * sizeof(SelectLds)), gshare, u, u < total, lane);
+
+    // Every wave has drained its stores. A workgroup's resources are released
+    // only when its last wave ends, so the others wait here for free; wave 0
+    // then reports the workgroup's pieces to the tickets of their batch
+    // elements, and the workgroup selects the outputs of any it completed.
+    lds_barrier();
+    const int P = a.beam * a.chunks;
+    const long long ulast = (ufirst + W < total ? ufirst + W : total) - 1;
+    const int bfirst = (int)(ufirst / P), blast = (int)(ulast / P); // at most W batch elements
+    if (wave == 0) {
+        const int bb = bfirst + lane;
+        bool done = false;
+        if (bb <= blast) {
+            const long long lo = (long long)bb * P > ufirst ? (long long)bb * P : ufirst;
+            const long long hi = (long long)(bb + 1) * P - 1 < ulast ? (long long)(bb + 1) * P - 1 : ulast;
+            const uint32_t n = (uint32_t)(hi - lo + 1);
+            const uint32_t prev =
+                __hip_atomic_fetch_add(&a.ticket[bb], n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            done = prev + n == (uint32_t)P; // every piece of bb has published
+        }
+        const uint64_t m = ballot(done);
+        if (lane == 0) {
+            g.todo[0] = (uint32_t)m;
+            g.todo[1] = (uint32_t)(m >> 32);
+        }
     }
-    __syncthreads();
-    if (!is_last)
+    lds_barrier();
+    uint64_t todo = ((uint64_t)g.todo[1] << 32) | g.todo[0];
+    if (todo == 0)
         return;
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    sort_batch(a, sm.t, b, tid);
+    const SortLds sm = sort_lds(lds + hdr, a); // the waves' selection LDS is free now
+    bool again = false;
+    while (todo != 0) {
+        const int i = __builtin_ctzll(todo);
+        todo &= todo - 1;
+        if (again)
+            lds_barrier(); // the previous batch element's LDS readers are done
+        again = true;
+        sort_batch(a, sm, g, bfirst + i, tid, W);
+    }
 }
 
 __global__ void zero_fill(uint32_t *p, size_t n)
@@ -969,6 +1157,12 @@ __global__ void zero_fill(uint32_t *p, size_t n)
 }
 
 } // namespace
+
+size_t group_lds_bytes(int waves, size_t sort_bytes)
+{
+    const size_t sel = (size_t)waves * sizeof(SelectLds);
+    return lds_header(waves) + (sel > sort_bytes ? sel : sort_bytes);
+}
 
 bool supported_vecs_per_thread(int nv)
 {
@@ -981,17 +1175,18 @@ bool supported_vecs_per_thread(int nv)
 }
 
 template <int DT>
-static hipError_t launch_dt(const StepArgs &a, int nv, hipStream_t s)
+static hipError_t launch_dt(const StepArgs &a, int nv, size_t lds, hipStream_t s)
 {
-    const dim3 grid((unsigned)((long long)a.B * a.beam * a.chunks)), block(kThreads);
+    const long long pieces = (long long)a.B * a.beam * a.chunks;
+    const dim3 grid((unsigned)((pieces + a.waves - 1) / a.waves)), block(kLanes * a.waves);
     const bool aligned = a.align_elems == 0 && a.V % Traits<DT>::epv == 0;
     switch (nv) {
-#define RTOPK_CASE(N)                                                              \
-    case N:                                                                        \
-        if (aligned)                                                               \
-            hipLaunchKernelGGL((rtopk_step<DT, N, true>), grid, block, 0, s, a);   \
-        else                                                                       \
-            hipLaunchKernelGGL((rtopk_step<DT, N, false>), grid, block, 0, s, a);  \
+#define RTOPK_CASE(N)                                                                \
+    case N:                                                                          \
+        if (aligned)                                                                 \
+            hipLaunchKernelGGL((rtopk_step<DT, N, true>), grid, block, lds, s, a);   \
+        else                                                                         \
+            hipLaunchKernelGGL((rtopk_step<DT, N, false>), grid, block, lds, s, a);  \
         break;
         RTOPK_CASE(1) RTOPK_CASE(2) RTOPK_CASE(3) RTOPK_CASE(4) RTOPK_CASE(6) RTOPK_CASE(8)
         RTOPK_CASE(10) RTOPK_CASE(12)
@@ -1002,15 +1197,15 @@ static hipError_t launch_dt(const StepArgs &a, int nv, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_step(const StepArgs &a, int dtype, int vecs_per_thread, hipStream_t stream)
+hipError_t launch_step(const StepArgs &a, int dtype, int vecs_per_thread, size_t lds_bytes, hipStream_t stream)
 {
     switch (dtype) {
     case 0:
-        return launch_dt<0>(a, vecs_per_thread, stream);
+        return launch_dt<0>(a, vecs_per_thread, lds_bytes, stream);
     case 1:
-        return launch_dt<1>(a, vecs_per_thread, stream);
+        return launch_dt<1>(a, vecs_per_thread, lds_bytes, stream);
     case 2:
-        return launch_dt<2>(a, vecs_per_thread, stream);
+        return launch_dt<2>(a, vecs_per_thread, lds_bytes, stream);
     default:
         return hipErrorInvalidValue;
     }

@@ -32,7 +32,7 @@ class RtopkError(RuntimeError):
 class rtopk_plan_t(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
         "chunks", "threads", "vecs_per_thread", "vecs_per_chunk", "elems_per_vec", "ngroups",
-        "chunk_limit", "queue_cap", "align_elems", "grid")]
+        "chunk_limit", "queue_cap", "align_elems", "grid", "sort_keys", "lds_bytes", "pieces_per_group")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

@@ -59,7 +59,7 @@ typedef enum {
     RTOPK_OK = 0,
     RTOPK_EINVAL = -1,  /* bad argument: NULL pointer, size < 1, k > beam*V, eos outside [0,V), ... */
     RTOPK_ENOTSUP = -2, /* valid but beyond the implementation limits: k > 64, beam > 512,
-                           B > 65536, beam * pieces-per-row > 2048 */
+                           B > 65536, beam * pieces-per-row > 3072 */
     RTOPK_ENOMEM = -3,  /* device allocation failed, or a caller workspace is too small */
     RTOPK_EHIP = -4     /* a HIP runtime call or kernel launch failed */
 } rtopk_status;
@@ -71,20 +71,23 @@ typedef enum {
 /*
  * How one call is decomposed (reported by rtopk_plan; the kernel uses it).
  * Each beam's row is split into `chunks` contiguous pieces of at most
- * `vecs_per_chunk` 16-byte vectors, one workgroup of `threads` threads per
- * piece, each thread holding `vecs_per_thread` vectors in registers. Within a
- * piece, element e (counted from the 16-byte-aligned address at or below the
+ * `vecs_per_chunk` 16-byte vectors, one wave64 (`threads` lanes) per piece,
+ * each lane holding `vecs_per_thread` vectors in registers; a workgroup holds
+ * `pieces_per_group` consecutive pieces and `grid` workgroups are launched. Within
+ * a piece, element e (counted from the 16-byte-aligned address at or below the
  * logits base pointer) belongs to group e mod `ngroups`; ngroups is k rounded
  * up to a power of two and the piece's threshold is the k-th largest group
  * maximum (the minimum when ngroups == k). Each piece publishes only its own
  * exact top-k by (logit desc, flat index asc) among the logits at or above its
  * threshold; up to `chunk_limit` of those are ranked in LDS, a piece with more
  * finds its top-k by k rounds of argmax. `queue_cap` = beam * chunks * k is the
- * candidate count per batch element.
+ * candidate count per batch element. The last piece of a batch element to
+ * finish selects its k outputs, ranking up to `sort_keys` survivors in LDS;
+ * `lds_bytes` is the dynamic LDS of one workgroup.
  */
 typedef struct {
     int chunks;          /* pieces per beam row (C) */
-    int threads;         /* threads per workgroup */
+    int threads;         /* threads per piece (one wave64) */
     int vecs_per_thread; /* 16-byte vectors held per thread */
     int vecs_per_chunk;  /* 16-byte vectors per piece */
     int elems_per_vec;   /* 4 for float32, 8 for float16/bfloat16 */
@@ -92,7 +95,10 @@ typedef struct {
     int chunk_limit;     /* candidates a piece ranks in LDS before switching to k argmax rounds */
     int queue_cap;       /* candidate slots per batch element (beam * chunks * k) */
     int align_elems;     /* misalignment of the logits base, in elements */
-    int grid;            /* workgroups launched: B * beam * chunks */
+    int grid;            /* workgroups launched: ceil(B * beam * chunks / pieces_per_group) */
+    int sort_keys;       /* survivors the per-batch selection ranks in LDS */
+    int lds_bytes;       /* dynamic LDS per workgroup */
+    int pieces_per_group; /* pieces (waves) per workgroup */
 } rtopk_plan_t;
 
 /*
@@ -161,7 +167,7 @@ int rtopk_plan(const void *logits, int B, int beam, int V, int k, int dtype, rto
  * Process-wide tuning overrides for experiments and tests (0 = automatic):
  * vecs_per_thread forces the 16-byte vectors each thread holds (one of
  * 1,2,3,4,6,8,10,12; others are rejected with RTOPK_EINVAL);
- * chunk_limit forces the per-piece LDS candidate limit (1..256, raised to k),
+ * chunk_limit forces the per-piece LDS candidate limit (1..64, raised to k),
  * which makes the argmax-rounds top-k path run whenever a piece has more
  * candidates.
  */

@@ -102,16 +102,19 @@ def test_plan_covers_rows(lib, shape):
         st, p = rtopk.rtopk_plan(base, B, beam, V, k, dt)
         assert st == 0, rtopk.rtopk_last_error()
         epv = 16 // esz
-        assert p.elems_per_vec == epv and p.threads == 256
+        assert p.elems_per_vec == epv and p.threads == 64
         assert p.align_elems == (mis % epv)
         span = (p.align_elems + V + epv - 1) // epv if (p.align_elems or V % epv) else V // epv
         # every vector a row touches lies in one of its pieces
         assert p.chunks * p.vecs_per_chunk >= span + (1 if (p.align_elems or V % epv) else 0) - 1
         assert p.vecs_per_chunk == p.threads * p.vecs_per_thread
-        assert p.grid == B * beam * p.chunks
+        assert p.grid == -(-B * beam * p.chunks // p.pieces_per_group)
         assert p.ngroups >= k and p.ngroups & (p.ngroups - 1) == 0 and p.ngroups < 2 * k
         assert p.chunk_limit >= k
         assert p.queue_cap == beam * p.chunks * k
+        assert p.sort_keys & (p.sort_keys - 1) == 0 and p.sort_keys <= 512
+        assert p.sort_keys >= min(512, p.queue_cap + beam)
+        assert p.lds_bytes >= 8 * p.sort_keys + 13 * beam + 13 * beam * p.chunks
         need = rtopk.rtopk_workspace_bytes(B, beam, V, k, dt)
         assert need >= 8 * B * p.queue_cap + 16 * B * beam * p.chunks
 
@@ -119,16 +122,16 @@ def test_plan_covers_rows(lib, shape):
 def test_overrides(lib):
     try:
         assert rtopk.rtopk_set_override(5, 0) == rtopk.RTOPK_EINVAL
-        assert rtopk.rtopk_set_override(0, 257) == rtopk.RTOPK_EINVAL
+        assert rtopk.rtopk_set_override(0, 65) == rtopk.RTOPK_EINVAL
         assert rtopk.rtopk_set_override(0, -1) == rtopk.RTOPK_EINVAL
         assert rtopk.rtopk_set_override(4, 1) == 0
         st, p = rtopk.rtopk_plan(None, 4, 4, 40000, 4, 1)
         assert st == 0 and p.vecs_per_thread == 4 and p.chunk_limit == 4  # raised to k
-        assert p.chunks == math.ceil(5000 / (256 * 4))
+        assert p.chunks == math.ceil(5000 / (64 * 4))
     finally:
         rtopk.rtopk_set_override(0, 0)
     st, p = rtopk.rtopk_plan(None, 4, 4, 40000, 4, 1)
-    assert p.chunk_limit == 256
+    assert p.chunk_limit == 64
 
 
 def test_release_without_workspaces_is_harmless(lib):

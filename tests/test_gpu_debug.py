@@ -1,16 +1,16 @@
 """Intermediate values of the HIP path checked against the oracle's own
 pass-1/pass-2 routines (LightSeq inference article, hierarchical decoding):
 
-* every piece's threshold equals the oracle's R-top-k of that piece under the
-  documented partition (element e of the aligned frame in group e mod
-  ngroups) -- bit for bit, since max/min are exact -- and never exceeds the
-  piece's k-th largest logit;
+* every piece's threshold lies between the oracle's R-top-k of the piece
+  itself and that of its whole row, under the documented partition (element e
+  of the aligned frame in group e mod ngroups) -- the pieces of a row that
+  share a workgroup pool their group maxima, and the R-top-k of any part of a
+  row containing the piece is in that range -- so it never exceeds the row's
+  k-th largest logit;
 * every piece's hit count equals the number of its logits >= threshold;
 * each piece publishes exactly its own top-min(hits, k) survivors by
   (logit desc, flat asc);
 * the merged log-sum-exp matches the oracle's float64 value;
-* for i.i.d. rows the mean number of survivors per piece matches the
-  inclusion-exclusion expectation.
 """
 import math
 
@@ -71,17 +71,18 @@ def check_intermediates(s, d, align):
                 continue
             assert abs(float(d["lse"][row]) - ref_lse[row]) <= 4e-6 * max(1.0, abs(ref_lse[row])), (b, j)
             rowx = s.logits[b, j]
+            T_row = oracle.threshold(rowx, s.dtype, plan["ngroups"], k, offset=(row * V + align) % plan["ngroups"])
+            kth_row = np.sort(x32[b, j].astype(np.float64))[::-1][k - 1] if V >= k else -math.inf
             for c, (lo, hi, off) in enumerate(piece_ranges(plan, row, V, align)):
                 u = row * C + c
                 T = float(d["T"][u])
                 if hi <= lo:
                     assert T == -math.inf and d["hits"][u] == 0
                     continue
-                T_ref = oracle.threshold(rowx, s.dtype, plan["ngroups"], k, offset=off, base=lo, n=hi - lo)
-                assert T == T_ref, (b, j, c, T, T_ref)
+                T_own = oracle.threshold(rowx, s.dtype, plan["ngroups"], k, offset=off, base=lo, n=hi - lo)
+                assert T_own <= T <= T_row, (b, j, c, T_own, T, T_row)
+                assert T <= kth_row  # never above the row's k-th largest logit
                 seg = x32[b, j, lo:hi].astype(np.float64)
-                if hi - lo >= k:
-                    assert T <= np.sort(seg)[::-1][k - 1]  # R-top-k never exceeds the k-th largest
                 hits = oracle.count_ge(rowx, s.dtype, T, base=lo, n=hi - lo)
                 assert int(d["hits"][u]) == hits, (b, j, c)
                 ts = np.arange(lo, hi)
@@ -136,36 +137,3 @@ def test_intermediates_overflow():
     finally:
         rtopk.rtopk_set_override(0, 0)
     assert check_intermediates(s, d, align) > 0  # some pieces took the exact top-k path
-
-
-def _expected_survivors(n, k):
-    """E[#{x >= R-top-k}] for n i.i.d. continuous values in k equal groups."""
-    g = n // k
-    total, j = 0.0, 0
-    while True:
-        p = 0.0
-        for i in range(1, k + 1):
-            ratio = 1.0
-            for m in range(j):
-                ratio *= (n - i * g - m) / (n - m)
-            p += (-1) ** (i + 1) * math.comb(k, i) * ratio
-        total += p
-        if p < 1e-12 or j > n:
-            return total
-        j += 1
-
-
-def test_survivor_statistics_match_closed_form():
-    s = synth.make_custom(64, 4, 4, 40000, synth.F32, seed=10, sigma=3.0)
-    d, align = run_debug(s)
-    plan = d["plan"]
-    sizes = {}
-    for row in range(s.B * s.beam):
-        for c, (lo, hi, _) in enumerate(piece_ranges(plan, row, s.V, align)):
-            sizes.setdefault(hi - lo, []).append(int(d["hits"][row * plan["chunks"] + c]))
-    for n, hits in sizes.items():
-        if len(hits) < 50 or n % 4:
-            continue
-        hits = np.array(hits, float)
-        exp = _expected_survivors(n, 4)
-        assert abs(hits.mean() - exp) < 5 * hits.std() / math.sqrt(len(hits)) + 1e-9, (n, hits.mean(), exp)

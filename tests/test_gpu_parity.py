@@ -58,7 +58,7 @@ EDGE = [
     (1, 6, 1, 5000, synth.BF16, {}),                 # k = 1, B = 1
     (2, 16, 64, 5000, synth.F16, {}),                # k = 64 (max), ngroups 64
     (3, 5, 5, 2999, synth.F32, {"n_finished": 4}),   # k = 5 -> 8 groups, finished beams
-    (1, 32, 8, 250000, synth.BF16, {}),              # 352 pieces per batch element (> 256 threads)
+    (1, 32, 8, 250000, synth.BF16, {}),              # 1312 pieces per batch element, 10496 published slots
     (2, 8, 8, 250000, synth.BF16, {"dist": "uniform", "sigma": 0.001}),  # ~70 ties per piece
     (4, 3, 3, 40000, synth.BF16, {"dist": "gumbel"}),
     (2, 4, 4, 40000, synth.F16, {"dist": "int"}),    # small integers: heavy exact ties
@@ -92,6 +92,16 @@ def test_constant_rows_tie_break_bf16():
     got = run(s)
     check(s, got)
     assert (got[0] == 0).all() and (got[1] == np.arange(8)[None, :]).all()
+
+
+def test_constant_rows_tie_break_f16_sorted_in_lds():
+    # every piece is all ties (its exact top-k comes from argmax rounds) and all
+    # 8 * 4 * 4 published candidates tie in score: more survivors than lanes
+    s = synth.make_custom(2, 4, 4, 40000, synth.F16, seed=13, const=0.5)
+    s.alive[:] = -1.0
+    got = run(s)
+    check(s, got)
+    assert (got[0] == 0).all() and (got[1] == np.arange(4)[None, :]).all()
 
 
 def test_duplicate_beams_tie_by_flat_index():
