@@ -158,6 +158,31 @@ __device__ __forceinline__ void drain_stores()
 // crosses an integer boundary before the truncation.
 __device__ __forceinline__ int small_div(int q, float inv_d) { return (int)(((float)q + 0.5f) * inv_d); }
 
+// ---------------------------------------------------------------- XCD placement
+// Workgroups are dispatched to the 8 XCDs round robin (workgroup w on XCD
+// w mod 8), and each XCD has its own L2. Workgroup w takes the pieces of
+// logical workgroup L(w), which groups consecutive logical workgroups -- hence
+// the pieces of a batch element -- on one XCD. Nothing relies on this for
+// correctness: the XCD a workgroup actually runs on is read from the hardware
+// and reported with its arrival (see rtopk_step).
+constexpr int kXcds = 8;
+__device__ __forceinline__ uint32_t xcc_id()
+{
+    uint32_t x;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+    return x & 0xfu;
+}
+__device__ __forceinline__ int logical_group(int w, int G)
+{
+    const int G8 = G - G % kXcds; // the last G mod 8 workgroups keep their index
+    return w < G8 ? (w % kXcds) * (G8 / kXcds) + w / kXcds : w;
+}
+__device__ __forceinline__ int xcd_of_logical(int L, int G)
+{
+    const int G8 = G - G % kXcds;
+    return L < G8 ? L / (G8 / kXcds) : L % kXcds;
+}
+
 // ---------------------------------------------------------------- wave primitives
 __device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 
@@ -782,13 +807,24 @@ struct SortLds {
 
 // Counters and reduction scratch of a workgroup, in front of its LDS.
 struct GroupLds {
-    uint32_t todo[2]; // batch elements whose ticket this workgroup completed
+    uint32_t todo[2];  // batch elements whose ticket this workgroup completed
+    uint32_t local[2]; // ... of which every piece was published on this workgroup's XCD
     uint32_t ns, ndbg;
     float fred[kMaxWaves];
     uint64_t kred[kMaxWaves];
 };
 
 static_assert(sizeof(GroupLds) <= kLdsShare, "GroupLds fits in front of the shared group maxima");
+
+// The selection runs on the whole workgroup (W waves) or on wave 0 alone (W
+// = 1, its siblings gone): a workgroup barrier or just the wave's own order.
+__device__ __forceinline__ void group_sync(int W)
+{
+    if (W == 1)
+        wave_sync();
+    else
+        lds_barrier();
+}
 
 __device__ __forceinline__ SortLds sort_lds(uint8_t *base, const StepArgs &a)
 {
@@ -812,11 +848,11 @@ __device__ __forceinline__ float block_max_f(float v, GroupLds &g, int lane, int
     v = wave_max_f(v);
     if (lane == 0)
         g.fred[wave] = v;
-    lds_barrier();
+    group_sync(W);
     float r = g.fred[0];
     for (int w = 1; w < W; ++w)
         r = fmaxf(r, g.fred[w]);
-    lds_barrier();
+    group_sync(W);
     return r;
 }
 __device__ __forceinline__ uint64_t block_max_u64(uint64_t v, GroupLds &g, int lane, int wave, int W)
@@ -824,17 +860,18 @@ __device__ __forceinline__ uint64_t block_max_u64(uint64_t v, GroupLds &g, int l
     v = wave_max_u64(v);
     if (lane == 0)
         g.kred[wave] = v;
-    lds_barrier();
+    group_sync(W);
     uint64_t r = g.kred[0];
     for (int w = 1; w < W; ++w)
         r = g.kred[w] > r ? g.kred[w] : r;
-    lds_barrier();
+    group_sync(W);
     return r;
 }
 
 // Descending bitonic sort of keys[0..P), P a power of two, whole workgroup.
 __device__ __forceinline__ void bitonic_desc(uint64_t *keys, int P, int tid, int nth)
 {
+    const int W = nth / kLanes;
     for (int size = 2; size <= P; size <<= 1) {
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
             for (int i = tid; i < (P >> 1); i += nth) {
@@ -847,7 +884,7 @@ __device__ __forceinline__ void bitonic_desc(uint64_t *keys, int P, int tid, int
                     keys[hi] = x;
                 }
             }
-            lds_barrier();
+            group_sync(W);
         }
     }
 }
@@ -912,7 +949,7 @@ __device__ __forceinline__ void sort_batch(const StepArgs &a, const SortLds &sm,
     // each beam's pieces merged pairwise at doubling distances: a fixed tree,
     // so the result does not depend on arrival order
     for (int stride = 1; stride < C; stride <<= 1) {
-        lds_barrier();
+        group_sync(W);
         for (int p = tid; p < P; p += nth) {
             const int c = p - small_div(p, invC) * C;
             if ((c & (2 * stride - 1)) == 0 && c + stride < C) {
@@ -924,7 +961,7 @@ __device__ __forceinline__ void sort_batch(const StepArgs &a, const SortLds &sm,
             }
         }
     }
-    lds_barrier();
+    group_sync(W);
     float bound = -INFINITY;
     for (int jj = tid; jj < beam; jj += nth) {
         const float alv = sm.alive[jj];
@@ -997,7 +1034,7 @@ __device__ __forceinline__ void sort_batch(const StepArgs &a, const SortLds &sm,
             offer(ok, key);
         }
     }
-    lds_barrier();
+    group_sync(W);
     const uint32_t ns = g.ns;
 
     // ---- D: the k best keys, in order
@@ -1026,7 +1063,7 @@ __device__ __forceinline__ void sort_batch(const StepArgs &a, const SortLds &sm,
             Pw <<= 1;
         for (int i = (int)ns + tid; i < Pw; i += nth)
             sm.keys[i] = 0ull; // below every real key
-        lds_barrier();
+        group_sync(W);
         bitonic_desc(sm.keys, Pw, tid, nth);
         for (int p = tid; p < a.k && (uint32_t)p < ns; p += nth)
             emit_out(p, sm.keys[p]);
@@ -1068,7 +1105,7 @@ __device__ __forceinline__ void sort_batch(const StepArgs &a, const SortLds &sm,
     // and slots need no clearing: every piece of an alive beam rewrites its
     // header before its arrival is counted, and slots are read only below a count.
     if (a.dbg_queue || a.dbg_count) {
-        lds_barrier();
+        group_sync(W);
         uint64_t *dq = a.dbg_queue ? a.dbg_queue + (long long)b * a.queue_cap : nullptr;
         for (int p = tid; p < P; p += nth) {
             const int n = (int)sm.pn[p];
@@ -1079,11 +1116,228 @@ __device__ __forceinline__ void sort_batch(const StepArgs &a, const SortLds &sm,
                     dq[base + e] = ((uint64_t)__float_as_uint(entry_x(ent)) << 32) | entry_flat(ent);
                 }
         }
-        lds_barrier();
+        group_sync(W);
         if (tid == 0 && a.dbg_count)
             a.dbg_count[b] = g.ndbg;
     }
     if (tid == 0)
+        put32(&a.ticket[b], 0u);
+}
+
+// DPP partner exchange for the in-register merge tree of the wave selection:
+// level 0 pairs lanes i ^ 1, level 1 pairs i ^ 2 (quad permutes), level 2
+// mirrors 8-lane halves, level 3 mirrors 16-lane rows. After levels 0..L-1
+// every lane of an aligned 2^L-lane segment has combined the whole segment.
+template <int LEVEL> __device__ __forceinline__ uint32_t dpp_partner(uint32_t v)
+{
+    constexpr int ctrl = LEVEL == 0 ? 0xb1 : LEVEL == 1 ? 0x4e : LEVEL == 2 ? 0x141 : 0x140;
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, ctrl, 0xf, 0xf, false);
+}
+template <int LEVEL> __device__ __forceinline__ void merge_level(float &m, float &s, float &t)
+{
+    const float m2 = __uint_as_float(dpp_partner<LEVEL>(__float_as_uint(m)));
+    const float s2 = __uint_as_float(dpp_partner<LEVEL>(__float_as_uint(s)));
+    const float t2 = __uint_as_float(dpp_partner<LEVEL>(__float_as_uint(t)));
+    lse_merge(m, s, m2, s2); // symmetric: both partners get the same bits
+    t = fmaxf(t, t2);
+}
+
+// The selection of batch element b by one wave, when its P <= 64 pieces fit
+// the lanes and its P*k <= 256 published slots fit 4 per lane: lane p owns
+// piece p and loads, with everything else, its beam's score and flag; each
+// beam's partials are merged by DPP butterflies over its lanes (C a power of
+// two <= 16) or by a fixed tree in LDS; survivors are ranked by ballot with
+// the count in a scalar register. No barriers, no LDS atomics.
+__device__ __forceinline__ void sort_batch_wave(const StepArgs &a, const SortLds &sm, int b, int lane, bool local)
+{
+    const int beam = a.beam, C = a.chunks, L = a.k;
+    const int P = beam * C, NS = P * L;
+    const uint64_t *slots = a.slots + (long long)b * NS;
+    const uint64_t *head = a.head + 2 * (long long)b * P;
+    const uint32_t K = (uint32_t)a.sort_keys;
+    const bool has_fin = a.finished != nullptr;
+    const uint8_t *finb = has_fin ? a.finished + (long long)b * beam : nullptr;
+    const float invC = 1.f / (float)C, invL = 1.f / (float)L;
+
+    // ---- one round trip: 4 slots per lane, this lane's piece header, its beam's
+    // flag and score. When every piece was published on this XCD, its L2 holds
+    // the data: loads that skip only the CU's L1 (sc0); otherwise
+    // device-coherent loads that skip the L2 too (sc1).
+    uint64_t spec[4];
+    const bool own = lane < P;
+    const int jp = own ? small_div(lane, invC) : 0; // this lane's beam
+    uint64_t h0 = 0, h1 = 0;
+    if (local) {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint64_t *>(slots), 0, 8 * NS, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint64_t *>(head), 0, 16 * P, 0x00020000);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) { // loads past num_records read 0
+            const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, 8 * (lane + r * kLanes), 0, 1);
+            spec[r] = ((uint64_t)v[1] << 32) | v[0];
+        }
+        const auto v0 = __builtin_amdgcn_raw_buffer_load_b64(rh, 16 * lane, 0, 1);
+        const auto v1 = __builtin_amdgcn_raw_buffer_load_b64(rh, 16 * lane + 8, 0, 1);
+        h0 = ((uint64_t)v0[1] << 32) | v0[0];
+        h1 = ((uint64_t)v1[1] << 32) | v1[0];
+    } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int gi = lane + r * kLanes;
+            spec[r] = gi < NS ? get64(&slots[gi]) : 0ull;
+        }
+        h0 = own ? get64(&head[2 * lane]) : 0ull;
+        h1 = own ? get64(&head[2 * lane + 1]) : 0ull;
+    }
+    const float alv = own ? a.alive[b * beam + jp] : 0.f;
+    const bool fin = own && has_fin && finb[jp] != 0;
+    float m = own ? __uint_as_float((uint32_t)h0) : -INFINITY;
+    float sum = own ? __uint_as_float((uint32_t)(h0 >> 32)) : 0.f;
+    float t = own ? __uint_as_float((uint32_t)h1) : -INFINITY;
+    const uint32_t pn = own && !fin ? (uint32_t)(h1 >> 32) : 0u;
+
+    // ---- each beam's partials, merged over its C lanes by a fixed tree
+    if ((C & (C - 1)) == 0 && C <= 16) {
+        if (C >= 2)
+            merge_level<0>(m, sum, t);
+        if (C >= 4)
+            merge_level<1>(m, sum, t);
+        if (C >= 8)
+            merge_level<2>(m, sum, t);
+        if (C >= 16)
+            merge_level<3>(m, sum, t);
+    } else {
+        if (own) {
+            sm.pm[lane] = m;
+            sm.ps[lane] = sum;
+            sm.pt[lane] = t;
+        }
+        for (int stride = 1; stride < C; stride <<= 1) {
+            wave_sync();
+            const int c = lane - jp * C;
+            if (own && (c & (2 * stride - 1)) == 0 && c + stride < C) {
+                float mm = sm.pm[lane], ss = sm.ps[lane];
+                lse_merge(mm, ss, sm.pm[lane + stride], sm.ps[lane + stride]);
+                sm.pm[lane] = mm;
+                sm.ps[lane] = ss;
+                sm.pt[lane] = fmaxf(sm.pt[lane], sm.pt[lane + stride]);
+            }
+        }
+        wave_sync();
+        if (own) {
+            m = sm.pm[jp * C];
+            sum = sm.ps[jp * C];
+            t = sm.pt[jp * C];
+        }
+        wave_sync(); // every lane has read before the tables below are rewritten
+    }
+    const float lse = fin ? __uint_as_float(0x7fc00000u) : (m + fast_log2(sum)) * kLn2; // NaN: finished
+    const float thr = fin ? INFINITY : t;
+    // at least k logits of a beam are >= thr, so at least k candidates score >= alive + (thr - lse)
+    const float bound = wave_max_f(own && !fin ? alv + (thr - lse) : -INFINITY);
+    // per-piece copies of the beam values, read by slot below (the per-piece
+    // arrays pm, ps, pt hold lse, thr, alive here); one finished flag per beam
+    float *plse = sm.pm, *pthr = sm.ps, *palive = sm.pt;
+    if (own) {
+        plse[lane] = lse;
+        pthr[lane] = thr;
+        palive[lane] = alv;
+        sm.pn[lane] = (uint8_t)pn;
+        if (lane == jp * C) {
+            sm.fin[jp] = (uint8_t)fin;
+            if (a.dbg_lse)
+                a.dbg_lse[b * beam + jp] = lse;
+        }
+    }
+    wave_sync();
+
+    // ---- survivors -> sort keys, ranked by ballot; ns is wave-uniform
+    uint32_t ns = 0;
+    auto offer = [&](bool ok, uint64_t key) {
+        const uint64_t mk = ballot(ok);
+        if (mk != 0) {
+            const uint32_t pos = ns + lane_prefix(mk);
+            if (ok && pos < K)
+                sm.keys[pos] = key;
+            ns += (uint32_t)__builtin_popcountll(mk);
+        }
+    };
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int gi = lane + r * kLanes;
+        bool ok = false;
+        uint64_t key = 0;
+        if (gi < NS) {
+            const int p = small_div(gi, invL);
+            if (gi - p * L < (int)sm.pn[p]) { // slots past a piece's count hold stale data
+                const float x = entry_x(spec[r]);
+                if (x >= pthr[p]) {
+                    const float sc = palive[p] + (x - plse[p]);
+                    key = score_key(sc, entry_flat(spec[r]));
+                    ok = sc >= bound;
+                }
+            }
+        }
+        offer(ok, key);
+    }
+    if (has_fin) { // a finished beam offers its end token at its running score
+        const int pj = lane * C; // the first piece of beam `lane`
+        const bool ok = lane < beam && sm.fin[lane] && palive[pj] >= bound;
+        offer(ok, ok ? score_key(palive[pj], (uint32_t)lane * (uint32_t)a.V + (uint32_t)a.eos_id) : 0ull);
+    }
+    wave_sync();
+
+    // ---- the k best keys, in order (ns <= P*k + beam <= 320)
+    auto emit_out = [&](int p, uint64_t key) {
+        const long long o = (long long)b * a.k + p;
+        const uint32_t flat = 0xffffffffu - (uint32_t)key;
+        const uint32_t jj = flat / (uint32_t)a.V;
+        a.out_beam[o] = (int32_t)jj;
+        a.out_token[o] = (int32_t)(flat - jj * (uint32_t)a.V);
+        a.out_score[o] = from_ord((uint32_t)(key >> 32));
+    };
+    if (ns <= (uint32_t)kLanes) {
+        if ((uint32_t)lane < ns) {
+            const uint64_t mine = sm.keys[lane];
+            uint32_t rank = 0;
+#pragma unroll 8
+            for (uint32_t i = 0; i < ns; ++i)
+                rank += sm.keys[i] > mine;
+            if (rank < (uint32_t)a.k)
+                emit_out((int)rank, mine);
+        }
+    } else {
+        int Pw = 2;
+        while ((uint32_t)Pw < ns)
+            Pw <<= 1;
+        for (int i = (int)ns + lane; i < Pw; i += kLanes)
+            sm.keys[i] = 0ull; // below every real key
+        wave_sync();
+        bitonic_desc(sm.keys, Pw, lane, kLanes);
+        for (int p = lane; p < a.k && (uint32_t)p < ns; p += kLanes)
+            emit_out(p, sm.keys[p]);
+    }
+    for (int p = (int)ns + lane; p < a.k; p += kLanes) { // padding: fewer than k candidates at all
+        const long long o = (long long)b * a.k + p;
+        a.out_beam[o] = -1;
+        a.out_token[o] = -1;
+        a.out_score[o] = -INFINITY;
+    }
+    if (a.dbg_queue || a.dbg_count) { // debug copies of every published candidate
+        const uint32_t before = wave_excl_scan_u32(pn, lane);
+        const uint32_t total = __builtin_amdgcn_readlane(before + pn, 63);
+        if (a.dbg_queue) {
+            uint64_t *dq = a.dbg_queue + (long long)b * a.queue_cap;
+            for (uint32_t e = 0; e < pn; ++e) {
+                const uint64_t ent = get64(&slots[(long long)lane * L + e]);
+                dq[before + e] = ((uint64_t)__float_as_uint(entry_x(ent)) << 32) | entry_flat(ent);
+            }
+        }
+        if (lane == 0 && a.dbg_count)
+            a.dbg_count[b] = total;
+    }
+    if (lane == 0)
         put32(&a.ticket[b], 0u);
 }
 
@@ -1096,7 +1350,8 @@ __global__ __launch_bounds__(kLanes *kMaxWaves) void rtopk_step(const StepArgs a
     const int W = a.waves;
     const size_t hdr = lds_header(W);
     const long long total = (long long)a.B * a.beam * a.chunks; // pieces
-    const long long ufirst = (long long)blockIdx.x * W;
+    const int LG = logical_group((int)blockIdx.x, (int)gridDim.x);
+    const long long ufirst = (long long)LG * W;
     const long long u = ufirst + wave;
     uint32_t *gshare = reinterpret_cast<uint32_t *>(lds + kLdsShare);
     // The barrier before the loads orders the clearing of the shared group
@@ -1117,36 +1372,58 @@ __global__ __launch_bounds__(kLanes *kMaxWaves) void rtopk_step(const StepArgs a
     const long long ulast = (ufirst + W < total ? ufirst + W : total) - 1;
     const int bfirst = (int)(ufirst / P), blast = (int)(ulast / P); // at most W batch elements
     if (wave == 0) {
+        // A ticket counts pieces in its low 20 bits and, above them, the
+        // arrivals from workgroups that did not run on the XCD expected for
+        // the batch element: if there were none, every piece of it was
+        // published through one L2 (that of the completing workgroup).
         const int bb = bfirst + lane;
-        bool done = false;
+        bool done = false, local = false;
         if (bb <= blast) {
             const long long lo = (long long)bb * P > ufirst ? (long long)bb * P : ufirst;
             const long long hi = (long long)(bb + 1) * P - 1 < ulast ? (long long)(bb + 1) * P - 1 : ulast;
             const uint32_t n = (uint32_t)(hi - lo + 1);
-            const uint32_t prev =
-                __hip_atomic_fetch_add(&a.ticket[bb], n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            done = prev + n == (uint32_t)P; // every piece of bb has published
+            const int xb = xcd_of_logical((int)(((long long)bb * P) / W), (int)gridDim.x);
+            const uint32_t inc = n + ((xcc_id() != (uint32_t)xb ? 1u : 0u) << 20);
+            const uint32_t now =
+                __hip_atomic_fetch_add(&a.ticket[bb], inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + inc;
+            done = (now & 0xfffffu) == (uint32_t)P; // every piece of bb has published
+            local = done && (now >> 20) == 0;
         }
-        const uint64_t m = ballot(done);
+        const uint64_t m = ballot(done), ml = ballot(local);
         if (lane == 0) {
             g.todo[0] = (uint32_t)m;
             g.todo[1] = (uint32_t)(m >> 32);
+            g.local[0] = (uint32_t)ml;
+            g.local[1] = (uint32_t)(ml >> 32);
         }
     }
     lds_barrier();
     uint64_t todo = ((uint64_t)g.todo[1] << 32) | g.todo[0];
+    const uint64_t local = ((uint64_t)g.local[1] << 32) | g.local[0];
     if (todo == 0)
         return;
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    // A batch element whose pieces and published slots fit one wave's lanes
+    // (up to 4 slots per lane) is selected by wave 0 alone, with no workgroup
+    // barriers in the way; larger ones by the whole workgroup.
+    int SW = W;
+    if (P <= kLanes && P * a.k <= 4 * kLanes) {
+        if (wave != 0)
+            return;
+        SW = 1;
+    }
     const SortLds sm = sort_lds(lds + hdr, a); // the waves' selection LDS is free now
     bool again = false;
     while (todo != 0) {
         const int i = __builtin_ctzll(todo);
         todo &= todo - 1;
         if (again)
-            lds_barrier(); // the previous batch element's LDS readers are done
+            group_sync(SW); // the previous batch element's LDS readers are done
         again = true;
-        sort_batch(a, sm, g, bfirst + i, tid, W);
+        if (SW == 1)
+            sort_batch_wave(a, sm, bfirst + i, lane, (local >> i) & 1);
+        else
+            sort_batch(a, sm, g, bfirst + i, tid, SW);
     }
 }
 
