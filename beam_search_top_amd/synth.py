@@ -25,7 +25,7 @@ round-to-nearest-even into the logit dtype):
                 (U(-1e-3, 1e-3)) and 128 Gumbel(0,1) beams; alive U(-50,0)
 
 The second argument of N(mu, sigma) is the standard deviation. Finished rows
-still hold random logits; a correct step never reads them.
+still hold random logits; a correct step never uses them.
 """
 from __future__ import annotations
 

@@ -199,6 +199,7 @@ def main():
         torch.cuda.synchronize()
 
     alg = algorithmic_bytes(s)
+    traffic = read_traffic(args.config)  # measured HBM bytes per launch, if taken on these sources
     achieved = alg / (ms_step * 1e-3) / 1e9
     cpu = None
     if not args.no_cpu:
@@ -229,7 +230,9 @@ def main():
         "hbm_frac": achieved / HBM_PEAK_GBPS,
         "algorithmic_bytes_per_step": alg,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": read_traffic(args.config)},
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": None if traffic is None else traffic / (ms_step * 1e-3) / 1e9},
+        "traffic_bytes_per_launch": traffic,
         "cpu_baseline": cpu,
         "kernel_sha": kernel_sha(),
     }

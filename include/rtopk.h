@@ -33,8 +33,10 @@
  *    lower flat index j*V + t. When fewer than k candidates exist (possible
  *    only when finished beams leave fewer than k), the tail is padded with
  *    beam = token = -1 and score = -inf.
- *  - Finished beams (finished_mask != 0) are not read: each offers the single
- *    continuation (j, eos_id) at its unchanged running score.
+ *  - A finished beam (finished_mask != 0) offers the single continuation
+ *    (j, eos_id) at its unchanged running score; its logits are never used.
+ *    (The kernel issues a piece's loads before the flag arrives, so a finished
+ *    row is still read once: that costs less than waiting for the flag.)
  *  - Scores are computed in float32: alive + (logit - lse), lse accumulated in
  *    float32 in a fixed order, so results are bit-reproducible across calls.
  *  - NaN or +inf logits, and alive beams whose logits are all -inf, are

@@ -119,6 +119,16 @@ def test_duplicate_beams_tie_by_flat_index():
                     assert got[2][b, q[0]] == got[2][b, p]
 
 
+def test_finished_rows_are_never_used():
+    # a finished row's logits may be loaded but must not reach any result:
+    # fill them with NaN and +inf (outside the contract for alive rows)
+    s = synth.make_custom(8, 4, 4, 40000, synth.F16, seed=31, sigma=3.0, n_finished=9)
+    fin = s.finished.astype(bool)
+    garbage = np.array([np.nan, np.inf], np.float16)
+    s.logits[fin] = garbage[np.arange(s.V) % 2][None, :]
+    check(s, run(s))
+
+
 def test_neg_inf_logits():
     s = synth.make_custom(2, 4, 4, 3000, synth.F32, seed=99, sigma=2.0)
     rng = np.random.default_rng(5)
