@@ -71,6 +71,7 @@ constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.69314718055994530942f;
 
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint32_t word(const uint4 &d, int i)
 {
@@ -512,7 +513,9 @@ __device__ __forceinline__ void select_piece(const StepArgs &a, SelectLds &sm, u
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     // Unconditional loads (index clamped into the piece) keep each load's
     // distance to its use visible to the waitcnt pass; empty or out-of-row
-    // slots are overwritten with -inf at their use, by selects.
+    // slots are overwritten with -inf at their use, by selects. The loads are
+    // non-temporal: the stream is read once, and without the hint it evicts
+    // from the L2s the code and workspace lines the end of the step needs.
     // (A wave past the last piece reads row 0's first piece and drops it: no
     // branch around the loads, so the waitcnt pass counts them exactly.)
     uint4 d[NV];
@@ -520,7 +523,8 @@ __device__ __forceinline__ void select_piece(const StepArgs &a, SelectLds &sm, u
 #pragma unroll
     for (int r = 0; r < NV; ++r) {
         const int q = pbeg + lane + r * kLanes;
-        d[r] = src[q < qlast ? q : qlast];
+        const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src) + (q < qlast ? q : qlast));
+        d[r] = make_uint4(w.x, w.y, w.z, w.w);
     }
     asm volatile("" : "+v"(fin)); // the test waits for the flag here, past the loads
     if (fin != 0)
@@ -1263,24 +1267,25 @@ __device__ __forceinline__ void sort_batch_wave(const StepArgs &a, const SortLds
             ns += (uint32_t)__builtin_popcountll(mk);
         }
     };
+    // the four table reads of every slot are independent (no nested tests),
+    // so their LDS latencies overlap
+    bool ok4[4];
+    uint64_t key4[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int gi = lane + r * kLanes;
-        bool ok = false;
-        uint64_t key = 0;
-        if (gi < NS) {
-            const int p = small_div(gi, invL);
-            if (gi - p * L < (int)sm.pn[p]) { // slots past a piece's count hold stale data
-                const float x = entry_x(spec[r]);
-                if (x >= pthr[p]) {
-                    const float sc = palive[p] + (x - plse[p]);
-                    key = score_key(sc, entry_flat(spec[r]));
-                    ok = sc >= bound;
-                }
-            }
-        }
-        offer(ok, key);
+        const int p = gi < NS ? small_div(gi, invL) : 0;
+        const uint32_t n = sm.pn[p];
+        const float th = pthr[p], al = palive[p], ls = plse[p];
+        const float x = entry_x(spec[r]);
+        const float sc = al + (x - ls);
+        key4[r] = score_key(sc, entry_flat(spec[r]));
+        // slots past a piece's count hold stale data
+        ok4[r] = gi < NS && (uint32_t)(gi - p * L) < n && x >= th && sc >= bound;
     }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        offer(ok4[r], key4[r]);
     if (has_fin) { // a finished beam offers its end token at its running score
         const int pj = lane * C; // the first piece of beam `lane`
         const bool ok = lane < beam && sm.fin[lane] && palive[pj] >= bound;
@@ -1289,10 +1294,12 @@ __device__ __forceinline__ void sort_batch_wave(const StepArgs &a, const SortLds
     wave_sync();
 
     // ---- the k best keys, in order (ns <= P*k + beam <= 320)
+    const bool small_flat = (long long)beam * a.V < (1 << 22);
+    const float invV = 1.f / (float)a.V;
     auto emit_out = [&](int p, uint64_t key) {
         const long long o = (long long)b * a.k + p;
         const uint32_t flat = 0xffffffffu - (uint32_t)key;
-        const uint32_t jj = flat / (uint32_t)a.V;
+        const uint32_t jj = small_flat ? (uint32_t)small_div((int)flat, invV) : flat / (uint32_t)a.V;
         a.out_beam[o] = (int32_t)jj;
         a.out_token[o] = (int32_t)(flat - jj * (uint32_t)a.V);
         a.out_score[o] = from_ord((uint32_t)(key >> 32));
