@@ -12,31 +12,54 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "librtopk.so")
-SOURCES = [os.path.join(CSRC, "rtopk_kernels.hip"), os.path.join(CSRC, "rtopk_host.cpp")]
+
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops off: no v_pk_{add,mul,fma}_f32 in the device code.
 # -fno-honor-nans: NaN logits are outside the contract, so
 # min/max need no NaN-quieting canonicalisation (infinities stay honoured).
 FLAGS = [
-    "-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=gfx950", "-ffp-contract=off",
+    "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-ffp-contract=off",
     "-fno-honor-nans",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
+KERNELS = os.path.join(CSRC, "rtopk_kernels.hip")
+HOST = os.path.join(CSRC, "rtopk_host.cpp")
+DTYPES = (0, 1, 2)  # the kernel source is compiled once per logit type, in parallel
+
+
+def _run(cmds, verbose):
+    procs = []
+    for cmd in cmds:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True))
+    failed = False
+    for p in procs:
+        out, _ = p.communicate()
+        if p.returncode != 0:
+            sys.stderr.write(out)
+            failed = True
+    if failed:
+        raise RuntimeError("hipcc failed to build librtopk.so")
 
 
 def build(verbose: bool = False, extra=()) -> str:
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [HIPCC, *FLAGS, *extra, *SOURCES, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed to build librtopk.so")
-    os.replace(tmp, LIB)
+    tag = f".tmp{os.getpid()}"
+    objs = [LIB + f".dt{d}{tag}.o" for d in DTYPES] + [LIB + f".host{tag}.o"]
+    cmds = [[HIPCC, *FLAGS, *extra, f"-DRTOPK_DTYPE={d}", "-c", KERNELS, "-o", o] for d, o in zip(DTYPES, objs)]
+    cmds.append([HIPCC, *FLAGS, *extra, "-c", HOST, "-o", objs[-1]])
+    tmp = LIB + tag
+    try:
+        _run(cmds, verbose)
+        _run([[HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp]], verbose)
+        os.replace(tmp, LIB)
+    finally:
+        for o in objs + [tmp]:
+            if os.path.exists(o):
+                os.remove(o)
     return LIB
 
 

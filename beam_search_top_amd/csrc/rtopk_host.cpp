@@ -37,6 +37,7 @@ int fail(int status, const char *fmt, ...)
 
 std::atomic<int> g_override_nv{0};
 std::atomic<int> g_override_limit{0};
+std::atomic<int> g_rowlocal{1};
 
 const int kVecsPerThread[] = {1, 2, 3, 4, 6, 8, 10, 12};
 // Most 16-byte vectors a lane holds without register spills and with >= 4
@@ -129,6 +130,11 @@ int make_plan(const void *logits, int B, int beam, int V, int k, int dtype, rtop
     // CU), of 4 when workgroups run in rounds and CUs must refill as they go.
     p->waves = rows * C <= kResidentPieces ? rtopk::kMaxWaves : 4;
     p->grid = ceil_div(rows * C, p->waves);
+    // Row-local: when a row's pieces divide the workgroup, workgroups hold
+    // whole rows and select them themselves; a batch element's rows then span
+    // at most maxl workgroups, which exchange one list of k keys each.
+    p->rowlocal = p->waves % C == 0 && g_rowlocal.load() ? 1 : 0;
+    p->maxl = (int)ceil_div((long long)beam * C, p->waves) + 1;
     if (p->grid > INT_MAX)
         return fail(RTOPK_ENOTSUP, "grid of %lld workgroups is too large", p->grid);
     if ((long long)beam * C > rtopk::kMaxPieces)
@@ -147,7 +153,7 @@ int make_plan(const void *logits, int B, int beam, int V, int k, int dtype, rtop
     // flag byte per beam
     const size_t pieces = (size_t)beam * (size_t)C;
     const size_t sort_lds = 8 * (size_t)p->sort_keys + 13 * pieces + 13 * (size_t)beam;
-    p->lds_bytes = (rtopk::group_lds_bytes(p->waves, sort_lds) + 15) & ~size_t(15);
+    p->lds_bytes = (rtopk::group_lds_bytes(p->waves, sort_lds, p->rowlocal != 0, k, p->maxl) + 15) & ~size_t(15);
 
     if (B > rtopk::kTicketCap)
         return fail(RTOPK_ENOTSUP, "B=%d exceeds the implementation limit %d", B, rtopk::kTicketCap);
@@ -157,9 +163,14 @@ int make_plan(const void *logits, int B, int beam, int V, int k, int dtype, rtop
     p->ws_ticket_off = off;
     off = align256(off + sizeof(uint32_t) * (size_t)rtopk::kTicketCap);
     p->ws_head_off = off;
-    off = align256(off + 16 * (size_t)rows * (size_t)C);
+    // piece headers (two words each), or row-local list counts
+    const size_t nhead = 2 * (size_t)rows * (size_t)C > (size_t)B * p->maxl ? 2 * (size_t)rows * (size_t)C
+                                                                            : (size_t)B * p->maxl;
+    off = align256(off + sizeof(uint64_t) * nhead);
     p->ws_slots_off = off;
-    off = align256(off + sizeof(uint64_t) * (size_t)B * (size_t)p->queue_cap);
+    // every piece's top-k, or row-local lists of k keys
+    const size_t nslot = (size_t)p->queue_cap > (size_t)p->maxl * k ? (size_t)p->queue_cap : (size_t)p->maxl * k;
+    off = align256(off + sizeof(uint64_t) * (size_t)B * nslot);
     p->ws_bytes = off;
     return RTOPK_OK;
 }
@@ -205,6 +216,8 @@ int enqueue(const rtopk::Plan &p, const void *logits, int dtype, const float *al
     a.queue_cap = p.queue_cap;
     a.sort_keys = p.sort_keys;
     a.waves = p.waves;
+    a.rowlocal = p.rowlocal;
+    a.maxl = p.maxl;
     uint8_t *w = (uint8_t *)ws;
     a.ticket = (uint32_t *)(w + p.ws_ticket_off);
     a.head = (uint64_t *)(w + p.ws_head_off);
@@ -217,7 +230,9 @@ int enqueue(const rtopk::Plan &p, const void *logits, int dtype, const float *al
     a.dbg_lse = dbg.lse;
     a.dbg_count = dbg.count;
     a.dbg_queue = dbg.queue;
-    hipError_t e = rtopk::launch_step(a, dtype, p.vecs_per_thread, p.lds_bytes, stream);
+    hipError_t e = dtype == RTOPK_F32   ? rtopk::launch_dtype<0>(a, p.vecs_per_thread, p.lds_bytes, stream)
+                   : dtype == RTOPK_F16 ? rtopk::launch_dtype<1>(a, p.vecs_per_thread, p.lds_bytes, stream)
+                                        : rtopk::launch_dtype<2>(a, p.vecs_per_thread, p.lds_bytes, stream);
     if (e != hipSuccess)
         return fail(RTOPK_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
     return RTOPK_OK;
@@ -362,6 +377,7 @@ int rtopk_plan(const void *logits, int B, int beam, int V, int k, int dtype, rto
     out->chunks = p.chunks;
     out->threads = rtopk::kLanes;
     out->pieces_per_group = p.waves;
+    out->row_local = p.rowlocal;
     out->vecs_per_thread = p.vecs_per_thread;
     out->vecs_per_chunk = p.vecs_per_chunk;
     out->elems_per_vec = p.epv;
@@ -386,11 +402,20 @@ int rtopk_set_override(int vecs_per_thread, int chunk_limit)
     return RTOPK_OK;
 }
 
+int rtopk_set_row_local(int enable)
+{
+    g_rowlocal.store(enable != 0 ? 1 : 0);
+    return RTOPK_OK;
+}
+
 const char *rtopk_last_error(void) { return g_err.c_str(); }
 
 void rtopk_release(void)
 {
     std::lock_guard<std::mutex> lock(g_ws_mu);
+    int cur = -1;
+    if (!g_ws.empty() && hipGetDevice(&cur) != hipSuccess)
+        cur = -1;
     for (auto &kv : g_ws) {
         if (kv.second.ptr) {
             (void)hipSetDevice(kv.first.first);
@@ -399,6 +424,8 @@ void rtopk_release(void)
         }
     }
     g_ws.clear();
+    if (cur >= 0)
+        (void)hipSetDevice(cur);
 }
 
 } // extern "C"

@@ -30,6 +30,8 @@ struct StepArgs {
     int queue_cap;                 // candidate slots per batch element = beam*chunks*k
     int sort_keys;                 // LDS sort keys of the per-batch selection (power of two)
     int waves;                     // pieces (waves) per workgroup, <= kMaxWaves
+    int rowlocal;                  // workgroups hold whole rows (chunks divides waves)
+    int maxl;                      // row-local: workgroup lists per batch element, at most
     // workspace; only the ticket region must be zero when a call starts
     uint32_t *ticket;              // [kTicketCap] arrivals, first B used
     uint64_t *head;                // [B*beam*chunks][2]: (max2 | sum << 32), (threshold | count << 32)
@@ -48,14 +50,16 @@ struct StepArgs {
 struct Plan {
     int elem_bytes, epv;
     int chunks, vecs_per_thread, vecs_per_chunk;
-    int ngroups, chunk_limit, queue_cap, align_elems, sort_keys, waves;
+    int ngroups, chunk_limit, queue_cap, align_elems, sort_keys, waves, rowlocal, maxl;
     long long grid;
     size_t lds_bytes;
     size_t ws_ticket_off, ws_head_off, ws_slots_off, ws_bytes;
 };
 
-// Enqueue the fused select + sort kernel. Returns a hipError_t.
-hipError_t launch_step(const StepArgs &a, int dtype, int vecs_per_thread, size_t lds_bytes, hipStream_t stream);
+// Enqueue the fused select + sort kernel for logits of type DT (0 float32,
+// 1 float16, 2 bfloat16). Returns a hipError_t.
+template <int DT>
+hipError_t launch_dtype(const StepArgs &a, int vecs_per_thread, size_t lds_bytes, hipStream_t stream);
 
 // Enqueue a zero fill of `bytes` (multiple of 4) at `p` (no hipMemsetAsync).
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream);
@@ -64,7 +68,15 @@ hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream);
 bool supported_vecs_per_thread(int nv);
 
 // Dynamic LDS of a workgroup of `waves` pieces whose per-batch selection
-// needs sort_bytes.
-size_t group_lds_bytes(int waves, size_t sort_bytes);
+// needs sort_bytes (and, row-local, keys for the workgroup's own selection).
+size_t group_lds_bytes(int waves, size_t sort_bytes, bool rowlocal, int k, int maxl);
+
+// Row-local workgroups: LDS keys of the workgroup's own selection (every
+// candidate of its pieces plus one per finished row) and of the final merge
+// (every list of a batch element).
+__host__ __device__ constexpr int rowlocal_keys(int waves, int k, int maxl)
+{
+    return waves * (k + 1) > maxl * k ? waves * (k + 1) : maxl * k;
+}
 
 } // namespace rtopk

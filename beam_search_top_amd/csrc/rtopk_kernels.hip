@@ -49,6 +49,12 @@
 //    and selects the k best survivors. It then puts the ticket back to zero;
 //    tickets live in a region of the workspace that no shape uses for
 //    anything else.
+// Compiled once per logit type (-DRTOPK_DTYPE=0 float32, 1 float16,
+// 2 bfloat16) so the instantiations build in parallel; the float32 unit also
+// holds the type-independent host helpers.
+#ifndef RTOPK_DTYPE
+#error "define RTOPK_DTYPE (0, 1 or 2)"
+#endif
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -474,13 +480,31 @@ __device__ __forceinline__ void opaque(uint4 &v)
 // with a neighbour row (kGeneral) are masked element by element.
 enum PieceMode { kAligned = 0, kGeneral = 1 };
 
-// LDS of the selection phase: the piece's candidates, one entry per lane.
+// LDS of the selection phase: the piece's candidates, one entry per lane;
+
+// The arrival counter of batch element b. Counters of consecutive batch
+// elements lie in different 64-byte lines (16 counters per line, b mod 4096
+// picks the line): their atomics then never queue behind each other's at the
+// memory side. A bijection on [0, kTicketCap).
+__device__ __forceinline__ uint32_t *ticket_of(const StepArgs &a, int b)
+{
+    static_assert(kTicketCap == 65536, "4096 lines of 16 counters");
+    return a.ticket + ((((uint32_t)b & 4095u) << 4) | ((uint32_t)b >> 12));
+}
+
+// in row-local workgroups also the piece's published top-k and header.
 struct SelectLds {
     uint64_t stage[kLanes];
+    uint64_t top[kMaxK];
+    float hm, hs, ht; // lse partial (max2, sum) and threshold
+    uint32_t hemit;   // keys in top
+    float ha;         // the row's running score
+    uint32_t hf;      // the row's finished flag
+    uint32_t pad[2];
 };
 static_assert(sizeof(SelectLds) % 16 == 0, "per-wave LDS regions stay 16-byte aligned");
 
-template <int DT, int NV, int MODE>
+template <int DT, int NV, int MODE, bool RL>
 __device__ __forceinline__ void select_piece(const StepArgs &a, SelectLds &sm, uint32_t *gshare_rows, long long u, bool valid,
                              int lane)
 {
@@ -510,6 +534,11 @@ __device__ __forceinline__ void select_piece(const StepArgs &a, SelectLds &sm, u
     // on their side of the test (a finished row reads its piece for nothing).
     const uint8_t *finp = !valid ? &kFlagConst[1] : a.finished != nullptr ? &a.finished[row] : &kFlagConst[0];
     uint32_t fin = *finp;
+    // row-local workgroups select their rows themselves: the row's score is
+    // loaded here too, its latency hidden under the stream like the flag's
+    float alv = 0.f;
+    if constexpr (RL)
+        alv = a.alive[row];
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     // Unconditional loads (index clamped into the piece) keep each load's
     // distance to its use visible to the waitcnt pass; empty or out-of-row
@@ -527,8 +556,17 @@ __device__ __forceinline__ void select_piece(const StepArgs &a, SelectLds &sm, u
         d[r] = make_uint4(w.x, w.y, w.z, w.w);
     }
     asm volatile("" : "+v"(fin)); // the test waits for the flag here, past the loads
-    if (fin != 0)
+    if (fin != 0) {
+        if (RL && lane == 0) { // an empty piece for the workgroup's own selection
+            sm.hm = -INFINITY;
+            sm.hs = 0.f;
+            sm.ht = -INFINITY;
+            sm.hemit = 0;
+            sm.ha = alv;
+            sm.hf = 1;
+        }
         return;
+    }
     // slots r < nfull hold valid vectors in every lane
     const int nfull = pend > pbeg ? (pend - pbeg) / kLanes : 0;
 
@@ -774,18 +812,46 @@ __device__ __forceinline__ void select_piece(const StepArgs &a, SelectLds &sm, u
     // element's top-k. Keys are distinct, so ranks are unique.
     uint64_t *mine = a.slots + (long long)u * a.k;
     const uint32_t emit = nst < (uint32_t)a.k ? nst : (uint32_t)a.k;
+    uint64_t key = 0;
+    uint32_t rank = ~0u;
     if ((uint32_t)lane < nst) {
-        const uint64_t key = sm.stage[lane];
-        uint32_t rank = lane;
+        key = sm.stage[lane];
+        rank = lane;
         if (nst > (uint32_t)a.k) {
             rank = 0;
 #pragma unroll 8
             for (uint32_t i = 0; i < nst; ++i)
                 rank += sm.stage[i] > key;
         }
-        if (rank < (uint32_t)a.k)
-            put64(&mine[rank], key);
     }
+    if (RL) {
+        // The workgroup holds whole rows and selects them itself: the piece's
+        // top-k and header stay in LDS; nothing to store or drain.
+        if (rank < (uint32_t)a.k)
+            sm.top[rank] = key;
+        if (lane == 0) {
+            sm.hm = pm;
+            sm.hs = ps;
+            sm.ht = T;
+            sm.hemit = emit;
+            sm.ha = alv;
+            sm.hf = 0;
+            if (a.dbg_T)
+                a.dbg_T[u] = T;
+            if (a.dbg_hits)
+                a.dbg_hits[u] = wn;
+        }
+        if (a.dbg_count && rank < (uint32_t)a.k) { // debug: append to the batch element's queue
+            const int b = row / a.beam;
+            const uint32_t pos = atomicAdd(&a.dbg_count[b], 1u);
+            if (a.dbg_queue)
+                a.dbg_queue[(long long)b * a.queue_cap + pos] =
+                    ((uint64_t)__float_as_uint(entry_x(key)) << 32) | entry_flat(key);
+        }
+        return;
+    }
+    if (rank < (uint32_t)a.k)
+        put64(&mine[rank], key);
     if (lane == 0) {
         put64(&a.head[2 * (long long)u], ((uint64_t)__float_as_uint(ps) << 32) | __float_as_uint(pm));
         put64(&a.head[2 * (long long)u + 1], ((uint64_t)emit << 32) | __float_as_uint(T));
@@ -1125,7 +1191,7 @@ __device__ __forceinline__ void sort_batch(const StepArgs &a, const SortLds &sm,
             a.dbg_count[b] = g.ndbg;
     }
     if (tid == 0)
-        put32(&a.ticket[b], 0u);
+        put32(ticket_of(a, b), 0u);
 }
 
 // DPP partner exchange for the in-register merge tree of the wave selection:
@@ -1345,38 +1411,214 @@ __device__ __forceinline__ void sort_batch_wave(const StepArgs &a, const SortLds
             a.dbg_count[b] = total;
     }
     if (lane == 0)
-        put32(&a.ticket[b], 0u);
+        put32(ticket_of(a, b), 0u);
 }
 
-template <int DT, int NV, bool ALIGNED>
-__global__ __launch_bounds__(kLanes *kMaxWaves) void rtopk_step(const StepArgs a)
-{
-    extern __shared__ __align__(16) uint8_t lds[];
-    GroupLds &g = *reinterpret_cast<GroupLds *>(lds);
-    const int tid = threadIdx.x, lane = tid & (kLanes - 1), wave = tid / kLanes;
-    const int W = a.waves;
-    const size_t hdr = lds_header(W);
-    const long long total = (long long)a.B * a.beam * a.chunks; // pieces
-    const int LG = logical_group((int)blockIdx.x, (int)gridDim.x);
-    const long long ufirst = (long long)LG * W;
-    const long long u = ufirst + wave;
-    uint32_t *gshare = reinterpret_cast<uint32_t *>(lds + kLdsShare);
-    // The barrier before the loads orders the clearing of the shared group
-    // maxima before any wave's use; after the loads it would hold every wave
-    // until the last of the workgroup's loads could issue.
-    for (int i = tid; i < W * kMaxK; i += kLanes * W)
-        gshare[i] = 0x007fffffu; // ord_bits(-inf)
-    lds_barrier();
-    select_piece<DT, NV, ALIGNED ? kAligned : kGeneral>(
-        a, *reinterpret_cast<SelectLds *>(lds + hdr + wave * sizeof(SelectLds)), gshare, u, u < total, lane);
+// ------------------------------------------------------------ row-local workgroups
+// When a row's pieces divide a workgroup, every workgroup holds whole rows and
+// can score them itself: wave 0 merges each row's partials (DPP over the C
+// lanes of its pieces), forms the workgroup's exact top-k of each batch
+// element it holds (candidates scored with the rows' own lse, filtered by the
+// rows' thresholds and the workgroup's bound), and either writes the outputs
+// (it held every row) or publishes that list of k keys. The batch element's
+// top-k restricted to one workgroup's rows lies in that workgroup's list, so
+// the last list to arrive merges exactly: one round trip of a few keys.
 
-    // Every wave has drained its stores. A workgroup's resources are released
-    // only when its last wave ends, so the others wait here for free; wave 0
-    // then reports the workgroup's pieces to the tickets of their batch
-    // elements, and the workgroup selects the outputs of any it completed.
-    lds_barrier();
+// Keys of this workgroup's selection: the k best of keys[0..n), then either
+// the outputs or the published list. `rank` of lane entries by counting when
+// n <= 64, else k rounds of wave argmax. Returns the number kept.
+__device__ __forceinline__ uint32_t wave_topk(uint64_t *keys, uint32_t n, int k, int lane, uint64_t *best_out)
+{
+    const uint32_t kept = n < (uint32_t)k ? n : (uint32_t)k;
+    if (n <= (uint32_t)kLanes) {
+        if ((uint32_t)lane < n) {
+            const uint64_t mine = keys[lane];
+            uint32_t rank = 0;
+#pragma unroll 8
+            for (uint32_t i = 0; i < n; ++i)
+                rank += keys[i] > mine;
+            if (rank < (uint32_t)k)
+                best_out[rank] = mine;
+        }
+    } else {
+        uint64_t prev = ~0ull;
+        for (uint32_t round = 0; round < kept; ++round) {
+            uint64_t best = 0;
+            for (uint32_t i = lane; i < n; i += kLanes) {
+                const uint64_t x = keys[i];
+                best = x < prev && x > best ? x : best;
+            }
+            best = wave_max_u64(best);
+            if (lane == 0)
+                best_out[round] = best;
+            prev = best;
+        }
+    }
+    wave_sync();
+    return kept;
+}
+
+__device__ __forceinline__ void emit_outputs(const StepArgs &a, int b, const uint64_t *best, uint32_t kept, int lane)
+{
+    for (int p = lane; p < a.k; p += kLanes) {
+        const long long o = (long long)b * a.k + p;
+        if ((uint32_t)p < kept) {
+            const uint64_t key = best[p];
+            const uint32_t flat = 0xffffffffu - (uint32_t)key;
+            const uint32_t jj = flat / (uint32_t)a.V;
+            a.out_beam[o] = (int32_t)jj;
+            a.out_token[o] = (int32_t)(flat - jj * (uint32_t)a.V);
+            a.out_score[o] = from_ord((uint32_t)(key >> 32));
+        } else { // fewer than k candidates at all
+            a.out_beam[o] = -1;
+            a.out_token[o] = -1;
+            a.out_score[o] = -INFINITY;
+        }
+    }
+}
+
+// Wave 0 of a row-local workgroup: its rows j0..j1 of batch element b (all
+// its pieces, np = (j1 - j0 + 1) * C <= W <= 16 of them, one per lane).
+// Returns true if the outputs of b still need the other workgroups' lists
+// (the list was published and this workgroup completed the ticket); the
+// caller then runs row_merge.
+__device__ __forceinline__ void row_select(const StepArgs &a, const SelectLds *wl, uint64_t *keys, uint64_t *best,
+                                           long long ufirst, int LG, int G, int b, int j0, int j1, int lane,
+                                           bool &done, bool &local)
+{
+    const int C = a.chunks, beam = a.beam, k = a.k;
+    const int nrows = j1 - j0 + 1, np = nrows * C;
+    const long long p0 = ((long long)b * beam + j0) * C; // first piece
+    const bool own = lane < np;
+    const int w = own ? (int)(p0 + lane - ufirst) : 0; // the wave that ran piece `lane`
+    const int jl = lane / C, j = j0 + jl;              // C is a power of two here
+    const float alv = own ? wl[w].ha : 0.f;
+    const bool fin = own && wl[w].hf != 0;
+    float m = own ? wl[w].hm : -INFINITY, sum = own ? wl[w].hs : 0.f, t = own ? wl[w].ht : -INFINITY;
+    const uint32_t emit = own && !fin ? wl[w].hemit : 0u;
+    if (C >= 2)
+        merge_level<0>(m, sum, t);
+    if (C >= 4)
+        merge_level<1>(m, sum, t);
+    if (C >= 8)
+        merge_level<2>(m, sum, t);
+    if (C >= 16)
+        merge_level<3>(m, sum, t);
+    const float lse = fin ? __uint_as_float(0x7fc00000u) : (m + fast_log2(sum)) * kLn2; // NaN: finished
+    const float thr = fin ? INFINITY : t;
+    // at least k logits of an alive row are >= thr: at least k candidates of
+    // this workgroup score >= its bound
+    const float bound = wave_max_f(own && !fin ? alv + (thr - lse) : -INFINITY);
+    if (a.dbg_lse && own && lane == jl * C)
+        a.dbg_lse[(long long)b * beam + j] = lse;
+
+    // survivors -> keys, by ballot (ns is wave-uniform)
+    uint32_t ns = 0;
+    auto offer = [&](bool ok, uint64_t key) {
+        const uint64_t mk = ballot(ok);
+        if (mk != 0) {
+            if (ok)
+                keys[ns + lane_prefix(mk)] = key;
+            ns += (uint32_t)__builtin_popcountll(mk);
+        }
+    };
+    const float invk = 1.f / (float)k;
+    for (int g0 = 0; g0 < np * k; g0 += kLanes) {
+        const int gi = g0 + lane;
+        const int p = gi < np * k ? small_div(gi, invk) : 0;
+        const int e = gi - p * k;
+        // the row values of piece p live in every lane of its row, e.g. lane p
+        const float plse = __shfl(lse, p), pthr = __shfl(thr, p), palv = __shfl(alv, p);
+        const uint32_t pe = (uint32_t)__shfl((int)emit, p);
+        const uint64_t ent = gi < np * k ? wl[p0 + p - ufirst].top[e] : 0ull;
+        const float x = entry_x(ent);
+        const float sc = palv + (x - plse);
+        const bool ok = gi < np * k && (uint32_t)e < pe && x >= pthr && sc >= bound;
+        offer(ok, score_key(sc, entry_flat(ent)));
+    }
+    if (a.finished != nullptr) { // a finished row offers its end token at its running score
+        const bool first = own && lane == jl * C;
+        const bool ok = first && fin && alv >= bound;
+        offer(ok, ok ? score_key(alv, (uint32_t)j * (uint32_t)a.V + (uint32_t)a.eos_id) : 0ull);
+    }
+    wave_sync();
+    const uint32_t kept = wave_topk(keys, ns, k, lane, best);
+
+    done = false;
+    local = false;
+    if (j0 == 0 && j1 == beam - 1) { // every row of b is here
+        emit_outputs(a, b, best, kept, lane);
+        return;
+    }
+    // publish this workgroup's list; the last list of b to arrive merges
+    const int Lf = (int)(((long long)b * beam * C) / a.waves);
+    const int idx = LG - Lf;
+    uint64_t *list = a.slots + ((long long)b * a.maxl + idx) * k;
+    for (int p = lane; p < (int)kept; p += kLanes)
+        put64(&list[p], best[p]);
+    if (lane == 0)
+        put64(&a.head[(long long)b * a.maxl + idx], kept);
+    drain_stores();
+    const int Ll = (int)((((long long)b + 1) * beam * C - 1) / a.waves);
+    uint32_t now = 0;
+    if (lane == 0) {
+        const int xb = xcd_of_logical(Lf, G);
+        const uint32_t inc = 1u + ((xcc_id() != (uint32_t)xb ? 1u : 0u) << 20);
+        now = __hip_atomic_fetch_add(ticket_of(a, b), inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + inc;
+    }
+    now = first_u32(now);
+    done = (now & 0xfffffu) == (uint32_t)(Ll - Lf + 1);
+    local = done && (now >> 20) == 0;
+}
+
+// The last list of batch element b arrived here: merge every list.
+__device__ __forceinline__ void row_merge(const StepArgs &a, uint64_t *keys, uint64_t *best, int b, int G,
+                                          int lane, bool local)
+{
+    const int C = a.chunks, beam = a.beam, k = a.k;
+    const int Lf = (int)(((long long)b * beam * C) / a.waves);
+    const int Ll = (int)((((long long)b + 1) * beam * C - 1) / a.waves);
+    const int nl = Ll - Lf + 1;
+    const uint64_t *lists = a.slots + (long long)b * a.maxl * k;
+    const uint64_t *counts = a.head + (long long)b * a.maxl;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    uint32_t n = 0;
+    for (int g0 = 0; g0 < nl * k; g0 += kLanes) {
+        const int gi = g0 + lane;
+        const int li = gi < nl * k ? gi / k : 0;
+        uint64_t cnt, ent;
+        if (local) { // every list was published on this XCD: through the L2 (sc0)
+            const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint64_t *>(lists), 0, 8 * nl * k, 0x00020000);
+            const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint64_t *>(counts), 0, 8 * nl, 0x00020000);
+            const auto v = __builtin_amdgcn_raw_buffer_load_b64(rl, 8 * gi, 0, 1);
+            const auto c2 = __builtin_amdgcn_raw_buffer_load_b64(rc, 8 * li, 0, 1);
+            ent = ((uint64_t)v[1] << 32) | v[0];
+            cnt = ((uint64_t)c2[1] << 32) | c2[0];
+        } else {
+            ent = gi < nl * k ? get64(&lists[gi]) : 0ull;
+            cnt = gi < nl * k ? get64(&counts[li]) : 0ull;
+        }
+        const bool ok = gi < nl * k && (uint64_t)(gi - li * k) < cnt;
+        const uint64_t mk = ballot(ok);
+        if (ok)
+            keys[n + lane_prefix(mk)] = ent;
+        n += (uint32_t)__builtin_popcountll(mk);
+    }
+    wave_sync();
+    const uint32_t kept = wave_topk(keys, n, k, lane, best);
+    emit_outputs(a, b, best, kept, lane);
+    if (lane == 0)
+        put32(ticket_of(a, b), 0u);
+}
+
+// Per-piece publication: tickets count the pieces; the workgroup that
+// completes a batch element selects its outputs from every published list.
+__device__ __forceinline__ void rtopk_step_tail(const StepArgs &a, GroupLds &g, uint8_t *lds, size_t hdr, int tid,
+                                                int lane, int wave, int W, long long ufirst, long long ulast)
+{
     const int P = a.beam * a.chunks;
-    const long long ulast = (ufirst + W < total ? ufirst + W : total) - 1;
     const int bfirst = (int)(ufirst / P), blast = (int)(ulast / P); // at most W batch elements
     if (wave == 0) {
         // A ticket counts pieces in its low 20 bits and, above them, the
@@ -1392,7 +1634,7 @@ __global__ __launch_bounds__(kLanes *kMaxWaves) void rtopk_step(const StepArgs a
             const int xb = xcd_of_logical((int)(((long long)bb * P) / W), (int)gridDim.x);
             const uint32_t inc = n + ((xcc_id() != (uint32_t)xb ? 1u : 0u) << 20);
             const uint32_t now =
-                __hip_atomic_fetch_add(&a.ticket[bb], inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + inc;
+                __hip_atomic_fetch_add(ticket_of(a, bb), inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + inc;
             done = (now & 0xfffffu) == (uint32_t)P; // every piece of bb has published
             local = done && (now >> 20) == 0;
         }
@@ -1434,17 +1676,74 @@ __global__ __launch_bounds__(kLanes *kMaxWaves) void rtopk_step(const StepArgs a
     }
 }
 
+// RL: row-local workgroups (chunks divides waves), a separate instantiation so
+// that neither tail's register needs weigh on the other.
+template <int DT, int NV, bool ALIGNED, bool RL>
+__global__ __launch_bounds__(kLanes *kMaxWaves) void rtopk_step(const StepArgs a)
+{
+    extern __shared__ __align__(16) uint8_t lds[];
+    GroupLds &g = *reinterpret_cast<GroupLds *>(lds);
+    const int tid = threadIdx.x, lane = tid & (kLanes - 1), wave = tid / kLanes;
+    const int W = a.waves;
+    const size_t hdr = lds_header(W);
+    const long long total = (long long)a.B * a.beam * a.chunks; // pieces
+    const int LG = logical_group((int)blockIdx.x, (int)gridDim.x);
+    const long long ufirst = (long long)LG * W;
+    const long long u = ufirst + wave;
+    uint32_t *gshare = reinterpret_cast<uint32_t *>(lds + kLdsShare);
+    // The barrier before the loads orders the clearing of the shared group
+    // maxima before any wave's use; after the loads it would hold every wave
+    // until the last of the workgroup's loads could issue.
+    for (int i = tid; i < W * kMaxK; i += kLanes * W)
+        gshare[i] = 0x007fffffu; // ord_bits(-inf)
+    lds_barrier();
+    select_piece<DT, NV, ALIGNED ? kAligned : kGeneral, RL>(
+        a, *reinterpret_cast<SelectLds *>(lds + hdr + wave * sizeof(SelectLds)), gshare, u, u < total, lane);
+
+    // Every wave has drained its stores. A workgroup's resources are released
+    // only when its last wave ends, so the others wait here for free; wave 0
+    // then reports the workgroup's pieces to the tickets of their batch
+    // elements, and the workgroup selects the outputs of any it completed.
+    lds_barrier();
+    const long long ulast = (ufirst + W < total ? ufirst + W : total) - 1;
+    if constexpr (RL) {
+        if (wave != 0)
+            return;
+        const SelectLds *wl = reinterpret_cast<const SelectLds *>(lds + hdr);
+        uint64_t *keys = reinterpret_cast<uint64_t *>(lds + hdr + (size_t)W * sizeof(SelectLds));
+        uint64_t *best = keys + rowlocal_keys(W, a.k, a.maxl);
+        const int rfirst = (int)(ufirst / a.chunks), rlast = (int)(ulast / a.chunks);
+        for (int b = rfirst / a.beam; b <= rlast / a.beam; ++b) {
+            const int j0 = rfirst > b * a.beam ? rfirst - b * a.beam : 0;
+            const int j1 = rlast < (b + 1) * a.beam - 1 ? rlast - b * a.beam : a.beam - 1;
+            bool done, local;
+            row_select(a, wl, keys, best, ufirst, LG, (int)gridDim.x, b, j0, j1, lane, done, local);
+            if (done)
+                row_merge(a, keys, best, b, (int)gridDim.x, lane, local);
+            wave_sync();
+        }
+    } else {
+        rtopk_step_tail(a, g, lds, hdr, tid, lane, wave, W, ufirst, ulast);
+    }
+}
+
+#if RTOPK_DTYPE == 0
 __global__ void zero_fill(uint32_t *p, size_t n)
 {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
         p[i] = 0u;
 }
+#endif
 
 } // namespace
 
-size_t group_lds_bytes(int waves, size_t sort_bytes)
+#if RTOPK_DTYPE == 0
+
+size_t group_lds_bytes(int waves, size_t sort_bytes, bool rowlocal, int k, int maxl)
 {
     const size_t sel = (size_t)waves * sizeof(SelectLds);
+    if (rowlocal) // the waves' regions stay; then the selection's keys and its top-k
+        return lds_header(waves) + sel + 8 * ((size_t)rowlocal_keys(waves, k, maxl) + k);
     return lds_header(waves) + (sel > sort_bytes ? sel : sort_bytes);
 }
 
@@ -1458,43 +1757,6 @@ bool supported_vecs_per_thread(int nv)
     }
 }
 
-template <int DT>
-static hipError_t launch_dt(const StepArgs &a, int nv, size_t lds, hipStream_t s)
-{
-    const long long pieces = (long long)a.B * a.beam * a.chunks;
-    const dim3 grid((unsigned)((pieces + a.waves - 1) / a.waves)), block(kLanes * a.waves);
-    const bool aligned = a.align_elems == 0 && a.V % Traits<DT>::epv == 0;
-    switch (nv) {
-#define RTOPK_CASE(N)                                                                \
-    case N:                                                                          \
-        if (aligned)                                                                 \
-            hipLaunchKernelGGL((rtopk_step<DT, N, true>), grid, block, lds, s, a);   \
-        else                                                                         \
-            hipLaunchKernelGGL((rtopk_step<DT, N, false>), grid, block, lds, s, a);  \
-        break;
-        RTOPK_CASE(1) RTOPK_CASE(2) RTOPK_CASE(3) RTOPK_CASE(4) RTOPK_CASE(6) RTOPK_CASE(8)
-        RTOPK_CASE(10) RTOPK_CASE(12)
-#undef RTOPK_CASE
-    default:
-        return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-}
-
-hipError_t launch_step(const StepArgs &a, int dtype, int vecs_per_thread, size_t lds_bytes, hipStream_t stream)
-{
-    switch (dtype) {
-    case 0:
-        return launch_dt<0>(a, vecs_per_thread, lds_bytes, stream);
-    case 1:
-        return launch_dt<1>(a, vecs_per_thread, lds_bytes, stream);
-    case 2:
-        return launch_dt<2>(a, vecs_per_thread, lds_bytes, stream);
-    default:
-        return hipErrorInvalidValue;
-    }
-}
-
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream)
 {
     const size_t n = bytes / 4;
@@ -1504,6 +1766,36 @@ hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream)
     if (blocks == 0)
         blocks = 1;
     hipLaunchKernelGGL(zero_fill, dim3(blocks), dim3(256), 0, stream, (uint32_t *)p, n);
+    return hipGetLastError();
+}
+#endif
+
+template <>
+hipError_t launch_dtype<RTOPK_DTYPE>(const StepArgs &a, int nv, size_t lds, hipStream_t s)
+{
+    constexpr int DT = RTOPK_DTYPE;
+    const long long pieces = (long long)a.B * a.beam * a.chunks;
+    const dim3 grid((unsigned)((pieces + a.waves - 1) / a.waves)), block(kLanes * a.waves);
+    const bool aligned = a.align_elems == 0 && a.V % Traits<DT>::epv == 0;
+    const bool rl = a.rowlocal != 0;
+    switch (nv) {
+#define RTOPK_CASE(N)                                                                      \
+    case N:                                                                                \
+        if (aligned && rl)                                                                 \
+            hipLaunchKernelGGL((rtopk_step<DT, N, true, true>), grid, block, lds, s, a);   \
+        else if (aligned)                                                                  \
+            hipLaunchKernelGGL((rtopk_step<DT, N, true, false>), grid, block, lds, s, a);  \
+        else if (rl)                                                                       \
+            hipLaunchKernelGGL((rtopk_step<DT, N, false, true>), grid, block, lds, s, a);  \
+        else                                                                               \
+            hipLaunchKernelGGL((rtopk_step<DT, N, false, false>), grid, block, lds, s, a); \
+        break;
+        RTOPK_CASE(1) RTOPK_CASE(2) RTOPK_CASE(3) RTOPK_CASE(4) RTOPK_CASE(6) RTOPK_CASE(8)
+        RTOPK_CASE(10) RTOPK_CASE(12)
+#undef RTOPK_CASE
+    default:
+        return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

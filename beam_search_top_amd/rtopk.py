@@ -32,7 +32,8 @@ class RtopkError(RuntimeError):
 class rtopk_plan_t(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
         "chunks", "threads", "vecs_per_thread", "vecs_per_chunk", "elems_per_vec", "ngroups",
-        "chunk_limit", "queue_cap", "align_elems", "grid", "sort_keys", "lds_bytes", "pieces_per_group")]
+        "chunk_limit", "queue_cap", "align_elems", "grid", "sort_keys", "lds_bytes", "pieces_per_group",
+        "row_local")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -64,6 +65,8 @@ def load():
     L.rtopk_plan.restype = i32
     L.rtopk_set_override.argtypes = [i32, i32]
     L.rtopk_set_override.restype = i32
+    L.rtopk_set_row_local.argtypes = [i32]
+    L.rtopk_set_row_local.restype = i32
     L.rtopk_last_error.argtypes = []
     L.rtopk_last_error.restype = ctypes.c_char_p
     L.rtopk_release.argtypes = []
@@ -113,6 +116,10 @@ def rtopk_plan(logits, B, beam, V, k, dtype):
 
 def rtopk_set_override(vecs_per_thread, chunk_limit):
     return load().rtopk_set_override(vecs_per_thread, chunk_limit)
+
+
+def rtopk_set_row_local(enable):
+    return load().rtopk_set_row_local(enable)
 
 
 def rtopk_last_error():

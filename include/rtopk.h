@@ -85,7 +85,10 @@ typedef enum {
  * finds its top-k by k rounds of argmax. `queue_cap` = beam * chunks * k is the
  * candidate count per batch element. The last piece of a batch element to
  * finish selects its k outputs, ranking up to `sort_keys` survivors in LDS;
- * `lds_bytes` is the dynamic LDS of one workgroup.
+ * `lds_bytes` is the dynamic LDS of one workgroup. When `row_local` is set
+ * (chunks divides pieces_per_group), workgroups hold whole rows: each selects
+ * the exact top-k of the rows it holds in LDS, and only those lists of k
+ * keys are exchanged between the workgroups that share a batch element.
  */
 typedef struct {
     int chunks;          /* pieces per beam row (C) */
@@ -101,6 +104,7 @@ typedef struct {
     int sort_keys;       /* survivors the per-batch selection ranks in LDS */
     int lds_bytes;       /* dynamic LDS per workgroup */
     int pieces_per_group; /* pieces (waves) per workgroup */
+    int row_local;       /* 1: workgroups hold whole rows and select them in LDS */
 } rtopk_plan_t;
 
 /*
@@ -147,7 +151,8 @@ int rtopk_beam_step_ws(const void *logits, int dtype, const float *alive_scores,
  *   dbg_hits    device [B*beam*chunks] uint32: logits >= threshold in the piece (its
  *               R-top-k survivors, of which it publishes the best min(hits, k))
  *   dbg_lse     device [B*beam] float32: merged log-sum-exp (NaN for finished beams)
- *   dbg_count   device [B] uint32: candidates the pieces of each batch element emitted
+ *   dbg_count   device [B] uint32, zero-filled by the caller: candidates the pieces of
+ *               each batch element emitted
  *   dbg_queue   device [B*queue_cap] uint64: those candidates, entry = (float32 bits of
  *               the logit << 32) | (j*V + t), in no particular order; only the first
  *               dbg_count[b] of each batch element are defined
@@ -174,6 +179,14 @@ int rtopk_plan(const void *logits, int B, int beam, int V, int k, int dtype, rto
  * candidates.
  */
 int rtopk_set_override(int vecs_per_thread, int chunk_limit);
+
+/*
+ * Process-wide switch for tests and experiments: 0 turns the row-local
+ * workgroup selection off (every shape then takes the per-piece publication
+ * path), nonzero (the default) uses it wherever chunks divides the
+ * workgroup's pieces. Always RTOPK_OK.
+ */
+int rtopk_set_row_local(int enable);
 
 /* Thread-local description of the last non-OK status ("" if none). */
 const char *rtopk_last_error(void);

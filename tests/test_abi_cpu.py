@@ -114,7 +114,11 @@ def test_plan_covers_rows(lib, shape):
         assert p.queue_cap == beam * p.chunks * k
         assert p.sort_keys & (p.sort_keys - 1) == 0 and p.sort_keys <= 512
         assert p.sort_keys >= min(512, p.queue_cap + beam)
-        assert p.lds_bytes >= 8 * p.sort_keys + 13 * beam + 13 * beam * p.chunks
+        assert p.row_local == (1 if p.pieces_per_group % p.chunks == 0 else 0)
+        if p.row_local:  # the pieces' LDS regions, then every candidate of the workgroup
+            assert p.lds_bytes >= p.pieces_per_group * 8 * (64 + k + 1) + 8 * p.pieces_per_group * (k + 1)
+        else:
+            assert p.lds_bytes >= 8 * p.sort_keys + 13 * beam + 13 * beam * p.chunks
         need = rtopk.rtopk_workspace_bytes(B, beam, V, k, dt)
         assert need >= 8 * B * p.queue_cap + 16 * B * beam * p.chunks
 
@@ -132,6 +136,19 @@ def test_overrides(lib):
         rtopk.rtopk_set_override(0, 0)
     st, p = rtopk.rtopk_plan(None, 4, 4, 40000, 4, 1)
     assert p.chunk_limit == 64
+
+
+def test_row_local_switch(lib):
+    st, p = rtopk.rtopk_plan(None, 128, 4, 40000, 4, 1)
+    assert st == 0 and p.chunks == 8 and p.pieces_per_group == 16 and p.row_local == 1
+    try:
+        assert rtopk.rtopk_set_row_local(0) == 0
+        st, q = rtopk.rtopk_plan(None, 128, 4, 40000, 4, 1)
+        assert st == 0 and q.row_local == 0 and q.chunks == p.chunks and q.grid == p.grid
+    finally:
+        rtopk.rtopk_set_row_local(1)
+    st, p = rtopk.rtopk_plan(None, 3, 5, 1001, 3, 1)  # one piece per row: row-local too
+    assert st == 0 and p.row_local == (1 if p.pieces_per_group % p.chunks == 0 else 0)
 
 
 def test_release_without_workspaces_is_harmless(lib):

@@ -162,6 +162,28 @@ def test_forced_overflow_path_is_exact():
         rtopk.rtopk_set_override(0, 0)
 
 
+def test_row_local_and_published_paths_agree():
+    # shapes whose pieces per row divide the workgroup run row-local by
+    # default; the same shapes through the per-piece publication path
+    cases = [synth.make_step("b128"), synth.make_step("c32k"), synth.make_step("tiny"),
+             synth.make_custom(2, 16, 64, 5000, synth.F16, seed=77),
+             synth.make_custom(3, 5, 5, 2999, synth.F32, seed=78, n_finished=4),
+             synth.make_custom(5, 1, 7, 700, synth.F16, seed=79)]
+    for s in cases:
+        st, p = rtopk.rtopk_plan(None, s.B, s.beam, s.V, s.k, s.dtype)
+        assert st == 0 and p.row_local == 1, s.name
+    got_rl = [run(s) for s in cases]
+    assert rtopk.rtopk_set_row_local(0) == 0
+    try:
+        for s, g in zip(cases, got_rl):
+            print(f"[parity published] {s.name}", flush=True)
+            ref = check(s, run(s))
+            check(s, g)
+            del ref
+    finally:
+        rtopk.rtopk_set_row_local(1)
+
+
 @pytest.mark.parametrize("nv", [1, 2, 3, 4, 6, 8, 10, 12])
 def test_every_tile_variant(nv):
     cases = [synth.make_custom(4, 4, 4, 40000, synth.F16, seed=300 + nv, sigma=3.0, n_finished=1),
