@@ -135,8 +135,8 @@ int make_plan(const void *logits, int B, int beam, int V, int k, int dtype, rtop
     // at most maxl workgroups, which exchange one list of k keys each.
     p->rowlocal = p->waves % C == 0 && g_rowlocal.load() ? 1 : 0;
     p->maxl = (int)ceil_div((long long)beam * C, p->waves) + 1;
-    if (p->grid > INT_MAX)
-        return fail(RTOPK_ENOTSUP, "grid of %lld workgroups is too large", p->grid);
+    if (rows * C >= (1ll << 31)) // piece indices are 31-bit in the kernel
+        return fail(RTOPK_ENOTSUP, "%lld pieces are too many", rows * C);
     if ((long long)beam * C > rtopk::kMaxPieces)
         return fail(RTOPK_ENOTSUP, "beam*chunks = %lld exceeds the implementation limit %d (vocabulary too large "
                     "for this beam count)", (long long)beam * C, rtopk::kMaxPieces);
@@ -218,6 +218,10 @@ int enqueue(const rtopk::Plan &p, const void *logits, int dtype, const float *al
     a.waves = p.waves;
     a.rowlocal = p.rowlocal;
     a.maxl = p.maxl;
+    a.mc = rtopk::make_magic((uint32_t)p.chunks);
+    a.mb = rtopk::make_magic((uint32_t)beam);
+    a.mp = rtopk::make_magic((uint32_t)beam * (uint32_t)p.chunks);
+    a.mw = rtopk::make_magic((uint32_t)p.waves);
     uint8_t *w = (uint8_t *)ws;
     a.ticket = (uint32_t *)(w + p.ws_ticket_off);
     a.head = (uint64_t *)(w + p.ws_head_off);

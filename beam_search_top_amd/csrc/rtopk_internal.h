@@ -16,6 +16,23 @@ constexpr int kMaxPieces = 3072;    // pieces (beam * chunks) of one batch eleme
 constexpr int kMaxK = 64;
 constexpr int kTicketCap = 65536;   // batch elements the ticket region holds (B limit)
 
+// Division by a launch constant d >= 1 for dividends n < 2^31:
+// floor(n / d) = (n * mul) >> shr with shr = 31 + ceil(log2 d) and
+// mul = floor(2^shr / d) + 1 < 2^32 (Granlund and Montgomery, "Division by
+// invariant integers using multiplication", 1994, Theorem 4.2 with N = 31).
+struct Magic {
+    uint32_t mul, shr;
+};
+
+inline Magic make_magic(uint32_t d)
+{
+    uint32_t l = 0;
+    while ((1ull << l) < d)
+        ++l;
+    const uint32_t shr = 31 + l;
+    return Magic{(uint32_t)((1ull << shr) / d + 1), shr};
+}
+
 // Everything one launch needs, passed by value as the kernel argument.
 struct StepArgs {
     const uint8_t *logits_aligned; // logits base rounded down to 16 bytes
@@ -32,6 +49,7 @@ struct StepArgs {
     int waves;                     // pieces (waves) per workgroup, <= kMaxWaves
     int rowlocal;                  // workgroups hold whole rows (chunks divides waves)
     int maxl;                      // row-local: workgroup lists per batch element, at most
+    Magic mc, mb, mp, mw;          // division by chunks, beam, beam*chunks, waves
     // workspace; only the ticket region must be zero when a call starts
     uint32_t *ticket;              // [kTicketCap] arrivals, first B used
     uint64_t *head;                // [B*beam*chunks][2]: (max2 | sum << 32), (threshold | count << 32)

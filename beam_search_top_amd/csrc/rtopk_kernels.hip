@@ -181,8 +181,14 @@ __device__ __forceinline__ uint32_t xcc_id()
 }
 __device__ __forceinline__ int logical_group(int w, int G)
 {
-    const int G8 = G - G % kXcds; // the last G mod 8 workgroups keep their index
-    return w < G8 ? (w % kXcds) * (G8 / kXcds) + w / kXcds : w;
+    const uint32_t uw = (uint32_t)w, G8 = (uint32_t)G & ~(uint32_t)(kXcds - 1); // the last G mod 8 keep their index
+    return uw < G8 ? (int)((uw % kXcds) * (G8 / kXcds) + uw / kXcds) : w;
+}
+
+// floor(n / d) for n < 2^31, d given by its multiplier and shift (host-made)
+__device__ __forceinline__ uint32_t mdiv(uint32_t n, Magic m)
+{
+    return (uint32_t)(((uint64_t)n * m.mul) >> m.shr);
 }
 __device__ __forceinline__ int xcd_of_logical(int L, int G)
 {
@@ -482,6 +488,10 @@ enum PieceMode { kAligned = 0, kGeneral = 1 };
 
 // LDS of the selection phase: the piece's candidates, one entry per lane;
 
+// Cache policy of the logit loads: non-temporal (the NT bit of gfx950's
+// buffer instructions).
+constexpr int kBufNT = 2;
+
 // The arrival counter of batch element b. Counters of consecutive batch
 // elements lie in different 64-byte lines (16 counters per line, b mod 4096
 // picks the line): their atomics then never queue behind each other's at the
@@ -504,28 +514,30 @@ struct SelectLds {
 };
 static_assert(sizeof(SelectLds) % 16 == 0, "per-wave LDS regions stay 16-byte aligned");
 
+// u: the piece (wave-uniform), row0: the first row of the workgroup.
 template <int DT, int NV, int MODE, bool RL>
-__device__ __forceinline__ void select_piece(const StepArgs &a, SelectLds &sm, uint32_t *gshare_rows, long long u, bool valid,
-                             int lane)
+__device__ __forceinline__ void select_piece(const StepArgs &a, SelectLds &sm, uint32_t *gshare_rows, uint32_t u,
+                                             bool valid, uint32_t row0, int lane)
 {
     using Tr = Traits<DT>;
     constexpr int EPV = Tr::epv;
-    const int c = valid ? (int)(u % a.chunks) : 0;
-    const int row = valid ? (int)(u / a.chunks) : 0;
-    const int j = row % a.beam;
+    // Everything about the piece is wave-uniform scalar work, divisions by
+    // multiplication: the loads issue after a few instructions.
+    const uint32_t uu = valid ? u : row0 * (uint32_t)a.chunks;
+    const uint32_t row = mdiv(uu, a.mc);
+    const int c = (int)(uu - row * (uint32_t)a.chunks);
+    const int j = (int)(row - mdiv(row, a.mb) * (uint32_t)a.beam);
     // this row's shared group maxima (rows are counted from the workgroup's first)
-    const long long row0 = (long long)(u - (u % a.waves)) / a.chunks;
     uint32_t *gshare = gshare_rows + (row - row0) * kMaxK;
     // Vectors are counted in the 16-byte-aligned frame of the tensor; a row
     // starts `lead` elements into its first vector v0 and spans `span` vectors.
     // Everything per lane is 32-bit and relative to the row.
-    const long long e0 = (long long)row * a.V + a.align_elems;
-    const long long v0 = e0 / EPV;
+    const uint64_t e0 = (uint64_t)row * (uint32_t)a.V + (uint32_t)a.align_elems;
+    const uint64_t v0 = e0 / EPV;
     const int lead = (int)(e0 - v0 * EPV);
     const int span = (lead + a.V + EPV - 1) / EPV;
     const int pbeg = c * a.vecs_per_chunk; // piece start, vectors from v0
     const int pend = pbeg + a.vecs_per_chunk < span ? pbeg + a.vecs_per_chunk : span;
-    const uint4 *src = reinterpret_cast<const uint4 *>(a.logits_aligned) + v0;
     const uint32_t flat0 = (uint32_t)j * (uint32_t)a.V - (uint32_t)lead; // flat index of slot 0 of vector 0
 
     // The finished flag is loaded first but tested only once the piece's
@@ -540,19 +552,21 @@ __device__ __forceinline__ void select_piece(const StepArgs &a, SelectLds &sm, u
     if constexpr (RL)
         alv = a.alive[row];
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    // Unconditional loads (index clamped into the piece) keep each load's
-    // distance to its use visible to the waitcnt pass; empty or out-of-row
-    // slots are overwritten with -inf at their use, by selects. The loads are
-    // non-temporal: the stream is read once, and without the hint it evicts
-    // from the L2s the code and workspace lines the end of the step needs.
-    // (A wave past the last piece reads row 0's first piece and drops it: no
-    // branch around the loads, so the waitcnt pass counts them exactly.)
+    // Buffer loads through a descriptor that spans exactly the piece: a slot
+    // past its end reads 0 without touching memory, so the loads need no
+    // clamp and no 64-bit address per lane, and stay unconditional (each
+    // load's distance to its use visible to the waitcnt pass); such slots are
+    // overwritten with -inf at their use. A wave past the last piece gets an
+    // empty descriptor. The loads are non-temporal: the stream is read once,
+    // and without the hint it evicts from the L2s the code and workspace
+    // lines the end of the step needs.
+    const uint32_t nbytes = valid && pend > pbeg ? (uint32_t)(pend - pbeg) * 16u : 0u;
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(a.logits_aligned) + (v0 + (uint64_t)pbeg) * 16u, 0, nbytes, 0x00020000);
     uint4 d[NV];
-    const int qlast = pend - 1;
 #pragma unroll
     for (int r = 0; r < NV; ++r) {
-        const int q = pbeg + lane + r * kLanes;
-        const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src) + (q < qlast ? q : qlast));
+        const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rsrc, lane * 16, r * kLanes * 16, kBufNT);
         d[r] = make_uint4(w.x, w.y, w.z, w.w);
     }
     asm volatile("" : "+v"(fin)); // the test waits for the flag here, past the loads
@@ -1483,7 +1497,7 @@ __device__ __forceinline__ void emit_outputs(const StepArgs &a, int b, const uin
 // (the list was published and this workgroup completed the ticket); the
 // caller then runs row_merge.
 __device__ __forceinline__ void row_select(const StepArgs &a, const SelectLds *wl, uint64_t *keys, uint64_t *best,
-                                           long long ufirst, int LG, int G, int b, int j0, int j1, int lane,
+                                           uint32_t ufirst, int LG, int G, int b, int j0, int j1, int lane,
                                            bool &done, bool &local)
 {
     const int C = a.chunks, beam = a.beam, k = a.k;
@@ -1551,7 +1565,7 @@ __device__ __forceinline__ void row_select(const StepArgs &a, const SelectLds *w
         return;
     }
     // publish this workgroup's list; the last list of b to arrive merges
-    const int Lf = (int)(((long long)b * beam * C) / a.waves);
+    const int Lf = (int)mdiv((uint32_t)b * (uint32_t)(beam * C), a.mw);
     const int idx = LG - Lf;
     uint64_t *list = a.slots + ((long long)b * a.maxl + idx) * k;
     for (int p = lane; p < (int)kept; p += kLanes)
@@ -1559,7 +1573,7 @@ __device__ __forceinline__ void row_select(const StepArgs &a, const SelectLds *w
     if (lane == 0)
         put64(&a.head[(long long)b * a.maxl + idx], kept);
     drain_stores();
-    const int Ll = (int)((((long long)b + 1) * beam * C - 1) / a.waves);
+    const int Ll = (int)mdiv(((uint32_t)b + 1) * (uint32_t)(beam * C) - 1, a.mw);
     uint32_t now = 0;
     if (lane == 0) {
         const int xb = xcd_of_logical(Lf, G);
@@ -1576,8 +1590,8 @@ __device__ __forceinline__ void row_merge(const StepArgs &a, uint64_t *keys, uin
                                           int lane, bool local)
 {
     const int C = a.chunks, beam = a.beam, k = a.k;
-    const int Lf = (int)(((long long)b * beam * C) / a.waves);
-    const int Ll = (int)((((long long)b + 1) * beam * C - 1) / a.waves);
+    const int Lf = (int)mdiv((uint32_t)b * (uint32_t)(beam * C), a.mw);
+    const int Ll = (int)mdiv(((uint32_t)b + 1) * (uint32_t)(beam * C) - 1, a.mw);
     const int nl = Ll - Lf + 1;
     const uint64_t *lists = a.slots + (long long)b * a.maxl * k;
     const uint64_t *counts = a.head + (long long)b * a.maxl;
@@ -1616,10 +1630,10 @@ __device__ __forceinline__ void row_merge(const StepArgs &a, uint64_t *keys, uin
 // Per-piece publication: tickets count the pieces; the workgroup that
 // completes a batch element selects its outputs from every published list.
 __device__ __forceinline__ void rtopk_step_tail(const StepArgs &a, GroupLds &g, uint8_t *lds, size_t hdr, int tid,
-                                                int lane, int wave, int W, long long ufirst, long long ulast)
+                                                int lane, int wave, int W, uint32_t ufirst, uint32_t ulast)
 {
     const int P = a.beam * a.chunks;
-    const int bfirst = (int)(ufirst / P), blast = (int)(ulast / P); // at most W batch elements
+    const int bfirst = (int)mdiv(ufirst, a.mp), blast = (int)mdiv(ulast, a.mp); // at most W batch elements
     if (wave == 0) {
         // A ticket counts pieces in its low 20 bits and, above them, the
         // arrivals from workgroups that did not run on the XCD expected for
@@ -1631,7 +1645,7 @@ __device__ __forceinline__ void rtopk_step_tail(const StepArgs &a, GroupLds &g, 
             const long long lo = (long long)bb * P > ufirst ? (long long)bb * P : ufirst;
             const long long hi = (long long)(bb + 1) * P - 1 < ulast ? (long long)(bb + 1) * P - 1 : ulast;
             const uint32_t n = (uint32_t)(hi - lo + 1);
-            const int xb = xcd_of_logical((int)(((long long)bb * P) / W), (int)gridDim.x);
+            const int xb = xcd_of_logical((int)mdiv((uint32_t)bb * (uint32_t)P, a.mw), (int)gridDim.x);
             const uint32_t inc = n + ((xcc_id() != (uint32_t)xb ? 1u : 0u) << 20);
             const uint32_t now =
                 __hip_atomic_fetch_add(ticket_of(a, bb), inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + inc;
@@ -1683,13 +1697,15 @@ __global__ __launch_bounds__(kLanes *kMaxWaves) void rtopk_step(const StepArgs a
 {
     extern __shared__ __align__(16) uint8_t lds[];
     GroupLds &g = *reinterpret_cast<GroupLds *>(lds);
-    const int tid = threadIdx.x, lane = tid & (kLanes - 1), wave = tid / kLanes;
+    const int tid = threadIdx.x, lane = tid & (kLanes - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kLanes); // uniform: piece math stays scalar
     const int W = a.waves;
     const size_t hdr = lds_header(W);
-    const long long total = (long long)a.B * a.beam * a.chunks; // pieces
+    const uint32_t total = (uint32_t)a.B * (uint32_t)a.beam * (uint32_t)a.chunks; // pieces, < 2^31
     const int LG = logical_group((int)blockIdx.x, (int)gridDim.x);
-    const long long ufirst = (long long)LG * W;
-    const long long u = ufirst + wave;
+    const uint32_t ufirst = (uint32_t)LG * (uint32_t)W;
+    const uint32_t u = ufirst + (uint32_t)wave;
+    const uint32_t row0 = mdiv(ufirst, a.mc);
     uint32_t *gshare = reinterpret_cast<uint32_t *>(lds + kLdsShare);
     // The barrier before the loads orders the clearing of the shared group
     // maxima before any wave's use; after the loads it would hold every wave
@@ -1698,22 +1714,23 @@ __global__ __launch_bounds__(kLanes *kMaxWaves) void rtopk_step(const StepArgs a
         gshare[i] = 0x007fffffu; // ord_bits(-inf)
     lds_barrier();
     select_piece<DT, NV, ALIGNED ? kAligned : kGeneral, RL>(
-        a, *reinterpret_cast<SelectLds *>(lds + hdr + wave * sizeof(SelectLds)), gshare, u, u < total, lane);
+        a, *reinterpret_cast<SelectLds *>(lds + hdr + wave * sizeof(SelectLds)), gshare, u, u < total, row0, lane);
 
     // Every wave has drained its stores. A workgroup's resources are released
     // only when its last wave ends, so the others wait here for free; wave 0
     // then reports the workgroup's pieces to the tickets of their batch
     // elements, and the workgroup selects the outputs of any it completed.
     lds_barrier();
-    const long long ulast = (ufirst + W < total ? ufirst + W : total) - 1;
+    const uint32_t ulast = (ufirst + W < total ? ufirst + W : total) - 1;
     if constexpr (RL) {
         if (wave != 0)
             return;
         const SelectLds *wl = reinterpret_cast<const SelectLds *>(lds + hdr);
         uint64_t *keys = reinterpret_cast<uint64_t *>(lds + hdr + (size_t)W * sizeof(SelectLds));
         uint64_t *best = keys + rowlocal_keys(W, a.k, a.maxl);
-        const int rfirst = (int)(ufirst / a.chunks), rlast = (int)(ulast / a.chunks);
-        for (int b = rfirst / a.beam; b <= rlast / a.beam; ++b) {
+        const int rfirst = (int)row0, rlast = (int)mdiv(ulast, a.mc);
+        const int blast = (int)mdiv((uint32_t)rlast, a.mb);
+        for (int b = (int)mdiv((uint32_t)rfirst, a.mb); b <= blast; ++b) {
             const int j0 = rfirst > b * a.beam ? rfirst - b * a.beam : 0;
             const int j1 = rlast < (b + 1) * a.beam - 1 ? rlast - b * a.beam : a.beam - 1;
             bool done, local;
