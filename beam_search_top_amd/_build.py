@@ -18,9 +18,12 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # -packed-fp32-ops off: no v_pk_{add,mul,fma}_f32 in the device code.
 # -fno-honor-nans: NaN logits are outside the contract, so
 # min/max need no NaN-quieting canonicalisation (infinities stay honoured).
+# Atomic optimizer off: it rewrites the few-lane LDS maxima of the threshold
+# pool into a scalar loop over the active lanes, slower than the single
+# ds_max the hardware serialises by itself.
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-ffp-contract=off",
-    "-fno-honor-nans",
+    "-fno-honor-nans", "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
