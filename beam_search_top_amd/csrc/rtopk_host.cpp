@@ -53,6 +53,10 @@ constexpr long long kResidentPieces = 4096;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Workgroups of 16 pieces while the grid fits the GPU at once (one per CU),
+// of 4 when workgroups run in rounds and CUs must refill as they go.
+int waves_for(long long pieces) { return pieces <= kResidentPieces ? rtopk::kMaxWaves : 4; }
+
 long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
 int pow2_ceil(int x)
@@ -115,6 +119,24 @@ int make_plan(const void *logits, int B, int beam, int V, int k, int dtype, rtop
                 break;
             }
         C = ceil_div(span, (long long)rtopk::kLanes * nv);
+        // Prefer somewhat larger pieces when they make a row's pieces divide
+        // the workgroup: its rows are then selected inside it (row-local),
+        // which saves a cross-workgroup round trip per piece; at most half of
+        // the pieces are given up for it.
+        if (g_rowlocal.load() && waves_for(rows * C) % C != 0) {
+            for (int v : kVecsPerThread) {
+                if (v <= nv || v > nvmax)
+                    continue;
+                const long long c2 = ceil_div(span, (long long)rtopk::kLanes * v);
+                if (2 * c2 < C)
+                    break;
+                if (waves_for(rows * c2) % c2 == 0) {
+                    nv = v;
+                    C = c2;
+                    break;
+                }
+            }
+        }
     }
     p->vecs_per_thread = nv;
     p->chunks = (int)C;
@@ -126,9 +148,7 @@ int make_plan(const void *logits, int B, int beam, int V, int k, int dtype, rtop
     p->chunk_limit = lim > 0 ? lim : rtopk::kMaxChunkLimit;
     if (p->chunk_limit < k)
         p->chunk_limit = k; // a piece always may emit its own top-k
-    // Workgroups of 16 pieces while the grid fits the GPU at once (one per
-    // CU), of 4 when workgroups run in rounds and CUs must refill as they go.
-    p->waves = rows * C <= kResidentPieces ? rtopk::kMaxWaves : 4;
+    p->waves = waves_for(rows * C);
     p->grid = ceil_div(rows * C, p->waves);
     // Row-local: when a row's pieces divide the workgroup, workgroups hold
     // whole rows and select them themselves; a batch element's rows then span
