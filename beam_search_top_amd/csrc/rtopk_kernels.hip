@@ -705,28 +705,50 @@ __device__ __forceinline__ void select_piece(const StepArgs &a, SelectLds &sm, u
     // which some lane holds a hit (a wave-uniform branch, usually taken once
     // or twice per piece) is examined element by element. Hits are ranked by
     // ballot + mbcnt, so the count is wave-uniform and no atomics are needed.
+    // With T finite, slots outside the row or piece (set to -inf in pass 1)
+    // cannot reach it: a vector's elements are tested by independent
+    // compares straight into lane masks, and only the elements that hit
+    // somewhere are staged. T = -inf (a row without k finite logits) takes
+    // the element-by-element test with the explicit bounds.
     const uint32_t cap = (uint32_t)a.chunk_limit;
     uint32_t wn = 0;
     if (ballot(tmax >= T) != 0) {
         int qb0 = pbeg + lane; // opaque: keeps per-element index math inside this block
         asm volatile("" : "+v"(qb0));
+        const bool tfin = T > -INFINITY;
 #pragma unroll
         for (int r = 0; r < NV; ++r) {
             opaque(d[r]);
             if (ballot(Tr::any_ge(d[r], T)) != 0) {
                 const int q = qb0 + r * kLanes;
-                const bool inq = q < pend;
+                if (tfin) {
+                    uint64_t mk[EPV];
 #pragma unroll
-                for (int i = 0; i < EPV; ++i) {
-                    const float x = Tr::elem(d[r], i);
-                    const int t = q * EPV + i - lead;
-                    const bool h = x >= T && inq && (MODE != kGeneral || (t >= 0 && t < a.V));
-                    const uint64_t m = ballot(h);
-                    if (m != 0) {
-                        const uint32_t pos = wn + lane_prefix(m);
-                        if (h && pos < cap)
-                            sm.stage[pos] = score_key(x, flat0 + (uint32_t)(q * EPV + i));
-                        wn += (uint32_t)__builtin_popcountll(m);
+                    for (int i = 0; i < EPV; ++i)
+                        mk[i] = ballot(Tr::elem(d[r], i) >= T);
+#pragma unroll
+                    for (int i = 0; i < EPV; ++i) {
+                        if (mk[i] != 0) {
+                            const uint32_t pos = wn + lane_prefix(mk[i]);
+                            if (((mk[i] >> lane) & 1u) && pos < cap)
+                                sm.stage[pos] = score_key(Tr::elem(d[r], i), flat0 + (uint32_t)(q * EPV + i));
+                            wn += (uint32_t)__builtin_popcountll(mk[i]);
+                        }
+                    }
+                } else {
+                    const bool inq = q < pend;
+#pragma unroll
+                    for (int i = 0; i < EPV; ++i) {
+                        const float x = Tr::elem(d[r], i);
+                        const int t = q * EPV + i - lead;
+                        const bool h = x >= T && inq && (MODE != kGeneral || (t >= 0 && t < a.V));
+                        const uint64_t m = ballot(h);
+                        if (m != 0) {
+                            const uint32_t pos = wn + lane_prefix(m);
+                            if (h && pos < cap)
+                                sm.stage[pos] = score_key(x, flat0 + (uint32_t)(q * EPV + i));
+                            wn += (uint32_t)__builtin_popcountll(m);
+                        }
                     }
                 }
             }
