@@ -405,7 +405,7 @@ template <> struct Traits<1> { // float16, max kept on packed pairs
         half2v t = __builtin_elementwise_max(__builtin_elementwise_max(pair(d, 0), pair(d, 1)),
                                              __builtin_elementwise_max(pair(d, 2), pair(d, 3)));
         const _Float16 th = (_Float16)T;
-        return t.x >= th || t.y >= th;
+        return __builtin_fmaxf16(t.x, t.y) >= th; // one compare: its lane mask is the ballot
     }
 };
 
@@ -716,10 +716,24 @@ __device__ __forceinline__ void select_piece(const StepArgs &a, SelectLds &sm, u
         int qb0 = pbeg + lane; // opaque: keeps per-element index math inside this block
         asm volatile("" : "+v"(qb0));
         const bool tfin = T > -INFINITY;
+        // per vector, the lanes holding a hit: in row-local kernels all the
+        // (independent) compares first; the others, whose tail already fills
+        // the registers, test each vector as they go
+        uint64_t vm[NV];
+        if constexpr (RL) {
+#pragma unroll
+            for (int r = 0; r < NV; ++r) {
+                opaque(d[r]);
+                vm[r] = ballot(Tr::any_ge(d[r], T));
+            }
+        }
 #pragma unroll
         for (int r = 0; r < NV; ++r) {
-            opaque(d[r]);
-            if (ballot(Tr::any_ge(d[r], T)) != 0) {
+            if constexpr (!RL) {
+                opaque(d[r]);
+                vm[r] = ballot(Tr::any_ge(d[r], T));
+            }
+            if (vm[r] != 0) {
                 const int q = qb0 + r * kLanes;
                 if (tfin) {
                     uint64_t mk[EPV];
