@@ -432,6 +432,18 @@ int rtopk_set_row_local(int enable)
     return RTOPK_OK;
 }
 
+int rtopk_read_probe(const void *src, size_t bytes, uint32_t marker, uint32_t *out, void *stream)
+{
+    if (src == nullptr || out == nullptr)
+        return fail(RTOPK_EINVAL, "read probe: NULL pointer");
+    if ((uintptr_t)src % 16 != 0 || bytes % 16 != 0)
+        return fail(RTOPK_EINVAL, "read probe: src must be 16-byte aligned and bytes a multiple of 16");
+    const hipError_t e = rtopk::launch_read_probe(src, bytes, marker, out, (hipStream_t)stream);
+    if (e != hipSuccess)
+        return fail(RTOPK_EHIP, "read probe launch: %s", hipGetErrorString(e));
+    return RTOPK_OK;
+}
+
 const char *rtopk_last_error(void) { return g_err.c_str(); }
 
 void rtopk_release(void)

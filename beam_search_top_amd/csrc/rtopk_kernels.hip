@@ -1781,6 +1781,30 @@ __global__ __launch_bounds__(kLanes *kMaxWaves) void rtopk_step(const StepArgs a
 }
 
 #if RTOPK_DTYPE == 0
+// Plain streaming read (measurement aid): kReadVecs 16-byte vectors per lane,
+// consecutive lanes on consecutive vectors, all loads issued before any use.
+constexpr int kReadVecs = 10;
+constexpr int kReadThreads = 256;
+__global__ __launch_bounds__(kReadThreads) void read_probe(const u32x4 *src, size_t n16, uint32_t marker,
+                                                           uint32_t *out)
+{
+    const size_t base = (size_t)blockIdx.x * kReadThreads * kReadVecs + threadIdx.x;
+    u32x4 v[kReadVecs];
+#pragma unroll
+    for (int i = 0; i < kReadVecs; ++i) {
+        const size_t idx = base + (size_t)i * kReadThreads;
+        v[i] = idx < n16 ? __builtin_nontemporal_load(src + idx) : u32x4{0u, 0u, 0u, 0u};
+    }
+    bool hit = false;
+#pragma unroll
+    for (int i = 0; i < kReadVecs; ++i) {
+        const size_t idx = base + (size_t)i * kReadThreads;
+        hit |= idx < n16 && (v[i].x == marker || v[i].y == marker || v[i].z == marker || v[i].w == marker);
+    }
+    if (hit)
+        out[0] = 1u;
+}
+
 __global__ void zero_fill(uint32_t *p, size_t n)
 {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
@@ -1808,6 +1832,20 @@ bool supported_vecs_per_thread(int nv)
     default:
         return false;
     }
+}
+
+hipError_t launch_read_probe(const void *src, size_t bytes, uint32_t marker, uint32_t *out, hipStream_t stream)
+{
+    const size_t n16 = bytes / 16;
+    const size_t per = (size_t)kReadThreads * kReadVecs;
+    const size_t blocks = (n16 + per - 1) / per;
+    if (blocks == 0)
+        return hipSuccess;
+    if (blocks > 0x7fffffff)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(read_probe, dim3((unsigned)blocks), dim3(kReadThreads), 0, stream,
+                       static_cast<const u32x4 *>(src), n16, marker, out);
+    return hipGetLastError();
 }
 
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream)

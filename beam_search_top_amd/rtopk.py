@@ -67,6 +67,8 @@ def load():
     L.rtopk_set_override.restype = i32
     L.rtopk_set_row_local.argtypes = [i32]
     L.rtopk_set_row_local.restype = i32
+    L.rtopk_read_probe.argtypes = [vp, sz, ctypes.c_uint32, vp, vp]
+    L.rtopk_read_probe.restype = i32
     L.rtopk_last_error.argtypes = []
     L.rtopk_last_error.restype = ctypes.c_char_p
     L.rtopk_release.argtypes = []
@@ -120,6 +122,10 @@ def rtopk_set_override(vecs_per_thread, chunk_limit):
 
 def rtopk_set_row_local(enable):
     return load().rtopk_set_row_local(enable)
+
+
+def rtopk_read_probe(src, nbytes, marker, out, stream):
+    return load().rtopk_read_probe(src, nbytes, marker, out, stream)
 
 
 def rtopk_last_error():

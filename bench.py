@@ -67,6 +67,42 @@ def read_traffic(config):
         return None
 
 
+def read_ceiling(L, ptrs, nbytes, K, cur):
+    """Practical HBM ceiling: a plain streaming read (rtopk_read_probe) of the
+    step's algorithmic byte count, over the same rotating buffers, replayed
+    from a captured graph like the step."""
+    import torch
+    n = nbytes - nbytes % 16
+    out = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+
+    def probe(i, stream):
+        rc = L.rtopk_read_probe(ptrs[i % len(ptrs)], n, 0x7fc00001, out.data_ptr(), stream)
+        if rc != 0:
+            raise RuntimeError("read probe failed")
+
+    cur_s = cur.cuda_stream
+    for i in range(20):
+        probe(i, cur_s)
+    graph = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(cur)
+    with torch.cuda.graph(graph, stream=cs):
+        for i in range(100):
+            probe(i, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    reps = max(1, K // 100)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(cur)
+    for _ in range(reps):
+        graph.replay()
+    end.record(cur)
+    torch.cuda.synchronize()
+    us = start.elapsed_time(end) * 1e3 / (reps * 100)
+    gbps = n / (us * 1e-6) / 1e9
+    return {"us_per_launch": us, "bytes": n, "GBps": gbps, "frac_of_peak": gbps / HBM_PEAK_GBPS,
+            "kernel": "rtopk_read_probe (16-byte non-temporal loads, 10 per lane, nothing else)"}
+
+
 def cpu_baseline(s, seconds):
     import oracle
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
@@ -94,6 +130,7 @@ def main():
     ap.add_argument("--pool-mib", type=int, default=1024, help="distinct logit buffers rotated through")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-read-ceiling", action="store_true", help="skip the plain-read ceiling measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 256 MiB device copy (reference kernel for HBM counters)")
     args = ap.parse_args()
@@ -199,6 +236,7 @@ def main():
         torch.cuda.synchronize()
 
     alg = algorithmic_bytes(s)
+    ceiling = None if args.no_read_ceiling else read_ceiling(L, ptrs, alg, K, cur)
     traffic = read_traffic(args.config)  # measured HBM bytes per launch, if taken on these sources
     achieved = alg / (ms_step * 1e-3) / 1e9
     cpu = None
@@ -233,6 +271,8 @@ def main():
                      "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": None if traffic is None else traffic / (ms_step * 1e-3) / 1e9},
         "traffic_bytes_per_launch": traffic,
+        "read_ceiling": ceiling,
+        "frac_of_read_ceiling": None if ceiling is None else achieved / ceiling["GBps"],
         "cpu_baseline": cpu,
         "kernel_sha": kernel_sha(),
     }

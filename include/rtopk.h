@@ -188,6 +188,18 @@ int rtopk_set_override(int vecs_per_thread, int chunk_limit);
  */
 int rtopk_set_row_local(int enable);
 
+/*
+ * Measurement aid, not part of the selection: a plain streaming read that
+ * gives the practical HBM ceiling the selection kernel is compared with. It
+ * reads `bytes` bytes at `src` once with 16-byte non-temporal loads (ten per
+ * lane, 256-lane workgroups, one launch) and sets out[0] = 1 if any aligned
+ * 32-bit word equals `marker`; otherwise it writes nothing.
+ *   src     device, 16-byte aligned; bytes a multiple of 16 (else RTOPK_EINVAL)
+ *   out     device uint32[1], caller-owned
+ * Asynchronous on `stream`; allocates nothing.
+ */
+int rtopk_read_probe(const void *src, size_t bytes, uint32_t marker, uint32_t *out, void *stream);
+
 /* Thread-local description of the last non-OK status ("" if none). */
 const char *rtopk_last_error(void);
 

@@ -153,3 +153,12 @@ def test_row_local_switch(lib):
 
 def test_release_without_workspaces_is_harmless(lib):
     rtopk.rtopk_release()
+
+
+def test_read_probe_validation(lib):
+    # misaligned source, ragged size and NULL pointers are rejected before any launch
+    assert rtopk.rtopk_read_probe(0x1008, 64, 0, 0x2000, None) == rtopk.RTOPK_EINVAL
+    assert rtopk.rtopk_read_probe(0x1000, 72, 0, 0x2000, None) == rtopk.RTOPK_EINVAL
+    assert rtopk.rtopk_read_probe(None, 64, 0, 0x2000, None) == rtopk.RTOPK_EINVAL
+    assert rtopk.rtopk_read_probe(0x1000, 64, 0, None, None) == rtopk.RTOPK_EINVAL
+    assert "read probe" in rtopk.rtopk_last_error()
