@@ -1529,14 +1529,21 @@ __device__ __forceinline__ void emit_outputs(const StepArgs &a, int b, const uin
 
 // Wave 0 of a row-local workgroup: its rows j0..j1 of batch element b (all
 // its pieces, np = (j1 - j0 + 1) * C <= W <= 16 of them, one per lane).
-// Returns true if the outputs of b still need the other workgroups' lists
-// (the list was published and this workgroup completed the ticket); the
-// caller then runs row_merge.
-__device__ __forceinline__ void row_select(const StepArgs &a, const SelectLds *wl, uint64_t *keys, uint64_t *best,
-                                           uint32_t ufirst, int LG, int G, int b, int j0, int j1, int lane,
-                                           bool &done, bool &local)
+// Returns the number of keys of this workgroup's list (in `best`) and sets
+// `done` when this workgroup arrived last among those holding rows of b and
+// every other list is published; the caller then runs row_merge.
+__device__ __forceinline__ uint32_t row_select(const StepArgs &a, const SelectLds *wl, uint64_t *keys, uint64_t *best,
+                                           uint32_t ufirst, int LG, int b, int j0, int j1, int lane,
+                                           bool &done)
 {
     const int C = a.chunks, beam = a.beam, k = a.k;
+    // A batch element whose rows span several workgroups: report this
+    // workgroup's arrival first, so that the atomic's round trip overlaps the
+    // selection below. Low 16 bits count arrivals, high 16 bits publications.
+    const bool whole = j0 == 0 && j1 == beam - 1;
+    uint32_t arrived = 0;
+    if (!whole && lane == 0)
+        arrived = __hip_atomic_fetch_add(ticket_of(a, b), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int nrows = j1 - j0 + 1, np = nrows * C;
     const long long p0 = ((long long)b * beam + j0) * C; // first piece
     const bool own = lane < np;
@@ -1595,70 +1602,70 @@ __device__ __forceinline__ void row_select(const StepArgs &a, const SelectLds *w
     const uint32_t kept = wave_topk(keys, ns, k, lane, best);
 
     done = false;
-    local = false;
-    if (j0 == 0 && j1 == beam - 1) { // every row of b is here
+    if (whole) { // every row of b is here
         emit_outputs(a, b, best, kept, lane);
-        return;
+        return kept;
     }
-    // publish this workgroup's list; the last list of b to arrive merges
     const int Lf = (int)mdiv((uint32_t)b * (uint32_t)(beam * C), a.mw);
-    const int idx = LG - Lf;
-    uint64_t *list = a.slots + ((long long)b * a.maxl + idx) * k;
-    for (int p = lane; p < (int)kept; p += kLanes)
-        put64(&list[p], best[p]);
-    if (lane == 0)
-        put64(&a.head[(long long)b * a.maxl + idx], kept);
-    drain_stores();
     const int Ll = (int)mdiv(((uint32_t)b + 1) * (uint32_t)(beam * C) - 1, a.mw);
-    uint32_t now = 0;
-    if (lane == 0) {
-        const int xb = xcd_of_logical(Lf, G);
-        const uint32_t inc = 1u + ((xcc_id() != (uint32_t)xb ? 1u : 0u) << 20);
-        now = __hip_atomic_fetch_add(ticket_of(a, b), inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + inc;
+    const uint32_t nl = (uint32_t)(Ll - Lf + 1); // workgroups holding rows of b
+    arrived = first_u32(arrived);
+    if ((arrived & 0xffffu) + 1u < nl) {
+        // not the last to arrive: publish this workgroup's list, then count
+        // the publication once its stores are performed
+        uint64_t *list = a.slots + ((long long)b * a.maxl + (LG - Lf)) * k;
+        for (int p = lane; p < (int)kept; p += kLanes)
+            put64(&list[p], best[p]);
+        if (lane == 0)
+            put64(&a.head[(long long)b * a.maxl + (LG - Lf)], kept);
+        drain_stores();
+        if (lane == 0)
+            __hip_atomic_fetch_add(ticket_of(a, b), 1u << 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return kept;
     }
-    now = first_u32(now);
-    done = (now & 0xfffffu) == (uint32_t)(Ll - Lf + 1);
-    local = done && (now >> 20) == 0;
+    // The last to arrive merges. Every other workgroup of b arrived before
+    // it, so each is running its selection and will publish: wait until the
+    // nl - 1 publications are counted (usually already true at the arrival,
+    // else a few polls). The cap only bounds the loop; it is never reached.
+    uint32_t pub = arrived >> 16;
+    for (int spin = 0; pub + 1u < nl && spin < (1 << 22); ++spin) {
+        __builtin_amdgcn_s_sleep(2);
+        pub = first_u32(__hip_atomic_load(ticket_of(a, b), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) >> 16;
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    done = true;
+    return kept;
 }
 
-// The last list of batch element b arrived here: merge every list.
-__device__ __forceinline__ void row_merge(const StepArgs &a, uint64_t *keys, uint64_t *best, int b, int G,
-                                          int lane, bool local)
+// The last workgroup of batch element b to arrive merges its own list (in
+// LDS, `best`, `kept` keys) with the lists every other workgroup published.
+__device__ __forceinline__ void row_merge(const StepArgs &a, uint64_t *keys, uint64_t *best, uint32_t kept,
+                                          int b, int LG, int lane)
 {
     const int C = a.chunks, beam = a.beam, k = a.k;
     const int Lf = (int)mdiv((uint32_t)b * (uint32_t)(beam * C), a.mw);
     const int Ll = (int)mdiv(((uint32_t)b + 1) * (uint32_t)(beam * C) - 1, a.mw);
-    const int nl = Ll - Lf + 1;
+    const int nl = Ll - Lf + 1, self = LG - Lf;
     const uint64_t *lists = a.slots + (long long)b * a.maxl * k;
     const uint64_t *counts = a.head + (long long)b * a.maxl;
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    uint32_t n = 0;
+    if ((uint32_t)lane < kept)
+        keys[lane] = best[lane];
+    uint32_t n = kept;
     for (int g0 = 0; g0 < nl * k; g0 += kLanes) {
         const int gi = g0 + lane;
         const int li = gi < nl * k ? gi / k : 0;
-        uint64_t cnt, ent;
-        if (local) { // every list was published on this XCD: through the L2 (sc0)
-            const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
-                const_cast<uint64_t *>(lists), 0, 8 * nl * k, 0x00020000);
-            const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
-                const_cast<uint64_t *>(counts), 0, 8 * nl, 0x00020000);
-            const auto v = __builtin_amdgcn_raw_buffer_load_b64(rl, 8 * gi, 0, 1);
-            const auto c2 = __builtin_amdgcn_raw_buffer_load_b64(rc, 8 * li, 0, 1);
-            ent = ((uint64_t)v[1] << 32) | v[0];
-            cnt = ((uint64_t)c2[1] << 32) | c2[0];
-        } else {
-            ent = gi < nl * k ? get64(&lists[gi]) : 0ull;
-            cnt = gi < nl * k ? get64(&counts[li]) : 0ull;
-        }
-        const bool ok = gi < nl * k && (uint64_t)(gi - li * k) < cnt;
+        const bool rd = gi < nl * k && li != self;
+        const uint64_t ent = rd ? get64(&lists[gi]) : 0ull;
+        const uint64_t cnt = rd ? get64(&counts[li]) : 0ull;
+        const bool ok = rd && (uint64_t)(gi - li * k) < cnt;
         const uint64_t mk = ballot(ok);
         if (ok)
             keys[n + lane_prefix(mk)] = ent;
         n += (uint32_t)__builtin_popcountll(mk);
     }
     wave_sync();
-    const uint32_t kept = wave_topk(keys, n, k, lane, best);
-    emit_outputs(a, b, best, kept, lane);
+    const uint32_t nk = wave_topk(keys, n, k, lane, best);
+    emit_outputs(a, b, best, nk, lane);
     if (lane == 0)
         put32(ticket_of(a, b), 0u);
 }
@@ -1769,10 +1776,10 @@ __global__ __launch_bounds__(kLanes *kMaxWaves) void rtopk_step(const StepArgs a
         for (int b = (int)mdiv((uint32_t)rfirst, a.mb); b <= blast; ++b) {
             const int j0 = rfirst > b * a.beam ? rfirst - b * a.beam : 0;
             const int j1 = rlast < (b + 1) * a.beam - 1 ? rlast - b * a.beam : a.beam - 1;
-            bool done, local;
-            row_select(a, wl, keys, best, ufirst, LG, (int)gridDim.x, b, j0, j1, lane, done, local);
+            bool done;
+            const uint32_t kept = row_select(a, wl, keys, best, ufirst, LG, b, j0, j1, lane, done);
             if (done)
-                row_merge(a, keys, best, b, (int)gridDim.x, lane, local);
+                row_merge(a, keys, best, kept, b, LG, lane);
             wave_sync();
         }
     } else {
