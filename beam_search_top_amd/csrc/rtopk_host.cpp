@@ -432,6 +432,33 @@ int rtopk_set_row_local(int enable)
     return RTOPK_OK;
 }
 
+int rtopk_beam_reorder(const void *src, void *dst, long long nslabs, int B, int beam, long long row_bytes,
+                       const int32_t *beam_ids, int ld, void *stream)
+{
+    if (src == nullptr || dst == nullptr || beam_ids == nullptr)
+        return fail(RTOPK_EINVAL, "beam reorder: NULL pointer");
+    if (nslabs < 1 || B < 1 || beam < 1 || row_bytes < 1)
+        return fail(RTOPK_EINVAL, "beam reorder: sizes must be >= 1 (nslabs=%lld B=%d beam=%d row_bytes=%lld)",
+                    nslabs, B, beam, row_bytes);
+    if (ld < beam)
+        return fail(RTOPK_EINVAL, "beam reorder: ld=%d is below beam=%d", ld, beam);
+    const long long rows = (long long)B * beam;
+    if (rows > (1ll << 40) / nslabs || nslabs * rows > (1ll << 50) / row_bytes)
+        return fail(RTOPK_EINVAL, "beam reorder: cache size overflows");
+    const long long bytes = nslabs * rows * row_bytes;
+    const long long cpr = (row_bytes + rtopk::reorder_chunk_bytes() - 1) / rtopk::reorder_chunk_bytes();
+    if (nslabs * rows * cpr > 0x7fffffffLL)
+        return fail(RTOPK_EINVAL, "beam reorder: %lld chunks exceed one launch", nslabs * rows * cpr);
+    const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
+    if (s0 < d0 + (uintptr_t)bytes && d0 < s0 + (uintptr_t)bytes)
+        return fail(RTOPK_EINVAL, "beam reorder: source and destination overlap");
+    const hipError_t e = rtopk::launch_beam_reorder(src, dst, nslabs, B, beam, row_bytes, beam_ids, ld,
+                                                    (hipStream_t)stream);
+    if (e != hipSuccess)
+        return fail(RTOPK_EHIP, "beam reorder launch: %s", hipGetErrorString(e));
+    return RTOPK_OK;
+}
+
 int rtopk_read_probe(const void *src, size_t bytes, uint32_t marker, uint32_t *out, void *stream)
 {
     if (src == nullptr || out == nullptr)

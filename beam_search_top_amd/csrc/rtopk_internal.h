@@ -81,6 +81,10 @@ hipError_t launch_dtype(const StepArgs &a, int vecs_per_thread, size_t lds_bytes
 
 // Enqueue a zero fill of `bytes` (multiple of 4) at `p` (no hipMemsetAsync).
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream);
+// cache refresh (rtopk_reorder.hip)
+long long reorder_chunk_bytes();
+hipError_t launch_beam_reorder(const void *src, void *dst, long long nslabs, int B, int beam, long long row_bytes,
+                               const int32_t *ids, int ld, hipStream_t stream);
 hipError_t launch_read_probe(const void *src, size_t bytes, uint32_t marker, uint32_t *out, hipStream_t stream);
 
 // Templates instantiated for vecs_per_thread.

@@ -67,6 +67,8 @@ def load():
     L.rtopk_set_override.restype = i32
     L.rtopk_set_row_local.argtypes = [i32]
     L.rtopk_set_row_local.restype = i32
+    L.rtopk_beam_reorder.argtypes = [vp, vp, ctypes.c_longlong, i32, i32, ctypes.c_longlong, vp, i32, vp]
+    L.rtopk_beam_reorder.restype = i32
     L.rtopk_read_probe.argtypes = [vp, sz, ctypes.c_uint32, vp, vp]
     L.rtopk_read_probe.restype = i32
     L.rtopk_last_error.argtypes = []
@@ -122,6 +124,10 @@ def rtopk_set_override(vecs_per_thread, chunk_limit):
 
 def rtopk_set_row_local(enable):
     return load().rtopk_set_row_local(enable)
+
+
+def rtopk_beam_reorder(src, dst, nslabs, B, beam, row_bytes, beam_ids, ld, stream):
+    return load().rtopk_beam_reorder(src, dst, nslabs, B, beam, row_bytes, beam_ids, ld, stream)
 
 
 def rtopk_read_probe(src, nbytes, marker, out, stream):
@@ -201,6 +207,32 @@ def beam_step(logits, alive, finished=None, k=None, eos_id=2, workspace=None, ou
     else:
         _check(rtopk_beam_step_ws(*args, _ptr(workspace), workspace.numel() * workspace.element_size(), stream))
     return outs
+
+
+def beam_reorder(src, dst, beam_ids):
+    """Cache refresh on torch device tensors, on the current stream.
+
+    src, dst: contiguous [nslabs, B*beam, ...] tensors of one dtype (e.g. the
+    keys and values of every layer stacked along dim 0); beam_ids: [B, ld]
+    int32 with ld >= beam (rtopk_beam_step's beam ids with k = beam). New beam
+    j of batch element b takes the row of old beam beam_ids[b, j]; an id
+    outside [0, beam) leaves that row of dst as it was. Returns dst.
+    """
+    import torch
+    if src.shape != dst.shape or src.dtype != dst.dtype or src.device != dst.device:
+        raise ValueError("src and dst must have the same shape, dtype and device")
+    if not (src.is_contiguous() and dst.is_contiguous() and beam_ids.is_contiguous()):
+        raise ValueError("src, dst and beam_ids must be contiguous")
+    if beam_ids.dtype != torch.int32 or beam_ids.dim() != 2 or src.dim() < 2:
+        raise ValueError("beam_ids must be a [B, ld] int32 tensor and src at least 2-D")
+    B, ld = beam_ids.shape
+    if src.shape[1] % B != 0:
+        raise ValueError("src.shape[1] must be B * beam")
+    beam = src.shape[1] // B
+    row_bytes = (src[0, 0].numel() if src.dim() > 2 else 1) * src.element_size()
+    stream = torch.cuda.current_stream(src.device).cuda_stream
+    _check(rtopk_beam_reorder(_ptr(src), _ptr(dst), src.shape[0], B, beam, row_bytes, _ptr(beam_ids), ld, stream))
+    return dst
 
 
 def debug_step(logits, alive, finished=None, k=None, eos_id=2):

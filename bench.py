@@ -103,6 +103,77 @@ def read_ceiling(L, ptrs, nbytes, K, cur):
             "kernel": "rtopk_read_probe (16-byte non-temporal loads, 10 per lane, nothing else)"}
 
 
+def bench_reorder(args):
+    """Cache refresh after the selection (rtopk_beam_reorder): a beam-major
+    cache of 6 layers x {keys, values} (12 slabs) of B*beam = 128*4 rows of
+    16 heads x 32 positions x 64 dims fp16 (64 KiB per row, 384 MiB per
+    cache), reordered by seeded beam ids; two caches alternate as source and
+    destination, each larger than the 256 MB Infinity Cache. Algorithmic bytes
+    = every destination row written once + every distinct source row read
+    once (beams that continue the same old beam share its read)."""
+    import numpy as np
+    import torch
+
+    from beam_search_top_amd import rtopk
+    rtopk.load()
+    L = rtopk.load()
+    dev = torch.device("cuda:0")
+    nslabs, B, beam, heads, pos, dim = 12, 128, 4, 16, 32, 64
+    row_bytes = heads * pos * dim * 2
+    n = nslabs * B * beam * row_bytes
+    caches = [torch.empty(n, dtype=torch.uint8, device=dev) for _ in range(2)]
+    for c in caches:
+        c.random_(0, 256)
+    rng = np.random.default_rng(1007)
+    ids_h = rng.integers(0, beam, size=(B, beam)).astype(np.int32)
+    ids = torch.from_numpy(ids_h).to(dev)
+    distinct = sum(len(set(r.tolist())) for r in ids_h)  # source rows per slab actually needed
+    cur = torch.cuda.current_stream()
+
+    def step(i):
+        src, dst = caches[i % 2], caches[(i + 1) % 2]
+        rc = L.rtopk_beam_reorder(src.data_ptr(), dst.data_ptr(), nslabs, B, beam, row_bytes, ids.data_ptr(), beam,
+                                  cur.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(rtopk.rtopk_last_error())
+
+    def timed(fn, K):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(cur)
+        for i in range(K):
+            fn(i)
+        end.record(cur)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / K
+
+    K = max(1, min(args.steps, 400))
+    for i in range(max(2, min(args.warmup, 20))):
+        step(i)
+    ms = timed(step, K)
+    alg = n + nslabs * distinct * row_bytes
+    gbps = alg / (ms * 1e-3) / 1e9
+    # practical ceiling: a plain device copy of the same bytes (torch's copy kernel)
+    copy_ms = timed(lambda i: caches[(i + 1) % 2].copy_(caches[i % 2]), K)
+    copy_gbps = 2 * n / (copy_ms * 1e-3) / 1e9
+    line = {
+        "metric": "KV-cache beam reorder (cache refresh) GB/s, read + write, 1xMI355X",
+        "value": gbps, "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+        "config": {"workload": f"reorder_b128: {nslabs} slabs (6 layers x K/V) x B={B} x beam={beam} rows of "
+                               f"{heads}x{pos}x{dim} fp16 ({row_bytes} B), seeded beam ids",
+                   "slabs": nslabs, "B": B, "beam": beam, "row_bytes": row_bytes},
+        "algorithmic_bytes_per_step": alg,
+        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": None},
+        "copy_ceiling": {"GBps": copy_gbps, "ms": copy_ms,
+                         "kernel": "torch device copy_ of one whole cache (reads and writes every row once)"},
+        "distinct_source_rows": distinct, "rows": B * beam,
+        "frac_of_copy_ceiling": gbps / copy_gbps,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def cpu_baseline(s, seconds):
     import oracle
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
@@ -125,6 +196,8 @@ def main():
     ap.add_argument("--steps", type=int, default=5000)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", default="b128")
+    ap.add_argument("--path", default="select", choices=["select", "reorder"],
+                    help="select: the selection step (the default line); reorder: the cache refresh after it")
     ap.add_argument("--launch", default="graph", choices=["graph", "eager"],
                     help="replay the K launches from a captured HIP graph, or launch each from Python")
     ap.add_argument("--pool-mib", type=int, default=1024, help="distinct logit buffers rotated through")
@@ -138,6 +211,10 @@ def main():
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the selection step of a batch "
               "element needs no other GPU, and this build measures the one-GPU kernel.", file=sys.stderr)
         sys.exit(2)
+
+    if args.path == "reorder":
+        bench_reorder(args)
+        return
 
     import numpy as np
     import torch

@@ -141,3 +141,23 @@ def decode_f16(code: int) -> float:
 
 def decode_bf16(code: int) -> float:
     return _load().rtopk_oracle_decode_bf16(int(code))
+
+
+def beam_reorder(src, dst_before, beam_ids, nslabs, B, beam):
+    """Cache refresh by its definition: once the selection has chosen, for
+    batch element b, new beam j as a continuation of old beam beam_ids[b][j],
+    the decoder's cache rows follow their beams (the LightSeq inference
+    article ends the decode step with this cache update, after the
+    hierarchical selection). In every slab s (a layer's keys or values), row
+    b*beam + j of the result is row b*beam + beam_ids[b][j] of src; an id
+    outside [0, beam) (padding) leaves the row of dst_before. Arrays are raw
+    bytes, [nslabs][B*beam][row_bytes]; returns a new array."""
+    src = np.asarray(src, dtype=np.uint8).reshape(nslabs, B, beam, -1)
+    out = np.array(dst_before, dtype=np.uint8, copy=True).reshape(nslabs, B, beam, -1)
+    ids = np.asarray(beam_ids)
+    for b in range(B):
+        for j in range(beam):
+            i = int(ids[b, j])
+            if 0 <= i < beam:
+                out[:, b, j, :] = src[:, b, i, :]
+    return out.reshape(nslabs, B * beam, -1)
