@@ -9,12 +9,12 @@
 //
 // MI355X design: a pure HBM copy (read each selected row once, write each
 // destination row once), so no LDS and no MFMA. One workgroup of 256 lanes
-// moves one chunk of up to 16 KiB of one destination row: every lane issues
-// its four 16-byte non-temporal loads before its first store, so each wave
-// keeps 4 KiB in flight, and a launch at the cache sizes of a decoder step
-// has tens of thousands of workgroups to spread over the 256 CUs. The source
-// row is one scalar load per workgroup. Rows that are not 16-byte aligned (or
-// whose size is not a multiple of 16) take a byte-wise variant.
+// moves one chunk of up to 16 KiB of one source row to every destination row
+// that takes it: every lane issues its four 16-byte non-temporal loads before
+// its first store, so each wave keeps 4 KiB in flight, and a launch at the
+// cache sizes of a decoder step has tens of thousands of workgroups to spread
+// over the 256 CUs. The beam ids are scalar loads. Rows that are not 16-byte
+// aligned (or whose size is not a multiple of 16) take a byte-wise variant.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -30,8 +30,11 @@ constexpr long long kReorderChunk = (long long)kReorderThreads * kReorderVecs * 
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// Workgroup w moves chunk c = w mod cpr of destination row r = w / cpr,
-// r = (s * B + b) * beam + j.
+// Workgroup w moves chunk c = w mod cpr of source row r = w / cpr,
+// r = (s * B + b) * beam + i, to every destination row of the same slab and
+// batch element whose beam continues old beam i: each source byte is read
+// from HBM once however many beams continue it, and a beam that no new beam
+// continues is not read at all.
 template <bool VEC>
 __global__ __launch_bounds__(kReorderThreads) void beam_reorder(const uint8_t *__restrict__ src,
                                                                 uint8_t *__restrict__ dst, long long row_bytes,
@@ -42,35 +45,50 @@ __global__ __launch_bounds__(kReorderThreads) void beam_reorder(const uint8_t *_
     const long long w = blockIdx.x;
     const long long r = w / cpr;
     const long long c = w - r * cpr;
-    const long long rb = r % rows_per_slab;       // b * beam + j
-    const long long b = rb / beam, j = rb - b * beam;
-    const int id = ids[b * ld + j];
-    if (id < 0 || id >= beam) // padding: the destination row keeps its contents
+    const long long rb = r % rows_per_slab; // b * beam + i
+    const long long b = rb / beam, i = rb - b * beam;
+    const int32_t *idb = ids + b * ld;
+    int first = -1; // the first destination beam that continues beam i
+    for (int j = 0; j < beam; ++j) {
+        if (idb[j] == (int32_t)i) {
+            first = j;
+            break;
+        }
+    }
+    if (first < 0) // no new beam continues old beam i
         return;
-    const long long from = r - j + id; // same slab and batch element, beam `id`
-    const uint8_t *s = src + from * row_bytes + c * kReorderChunk;
-    uint8_t *d = dst + r * row_bytes + c * kReorderChunk;
-    const long long left = row_bytes - c * kReorderChunk; // bytes of this row from the chunk start
+    const uint8_t *s = src + r * row_bytes + c * kReorderChunk;
+    uint8_t *drow = dst + (r - i) * row_bytes + c * kReorderChunk; // destination row of beam 0
+    const long long left = row_bytes - c * kReorderChunk;        // bytes of this row from the chunk start
     if constexpr (VEC) {
         const u32x4 *s4 = reinterpret_cast<const u32x4 *>(s);
-        u32x4 *d4 = reinterpret_cast<u32x4 *>(d);
         const long long n4 = left / 16;
         u32x4 v[kReorderVecs];
 #pragma unroll
-        for (int i = 0; i < kReorderVecs; ++i) {
-            const long long q = (long long)i * kReorderThreads + threadIdx.x;
-            v[i] = q < n4 ? __builtin_nontemporal_load(s4 + q) : u32x4{0u, 0u, 0u, 0u};
+        for (int q0 = 0; q0 < kReorderVecs; ++q0) {
+            const long long q = (long long)q0 * kReorderThreads + threadIdx.x;
+            v[q0] = q < n4 ? __builtin_nontemporal_load(s4 + q) : u32x4{0u, 0u, 0u, 0u};
         }
+        for (int j = first; j < beam; ++j) {
+            if (idb[j] != (int32_t)i)
+                continue;
+            u32x4 *d4 = reinterpret_cast<u32x4 *>(drow + (long long)j * row_bytes);
 #pragma unroll
-        for (int i = 0; i < kReorderVecs; ++i) {
-            const long long q = (long long)i * kReorderThreads + threadIdx.x;
-            if (q < n4)
-                __builtin_nontemporal_store(v[i], d4 + q);
+            for (int q0 = 0; q0 < kReorderVecs; ++q0) {
+                const long long q = (long long)q0 * kReorderThreads + threadIdx.x;
+                if (q < n4)
+                    __builtin_nontemporal_store(v[q0], d4 + q);
+            }
         }
     } else {
         const long long n = left < kReorderChunk ? left : kReorderChunk;
-        for (long long q = threadIdx.x; q < n; q += kReorderThreads)
-            d[q] = s[q];
+        for (int j = first; j < beam; ++j) {
+            if (idb[j] != (int32_t)i)
+                continue;
+            uint8_t *d = drow + (long long)j * row_bytes;
+            for (long long q = threadIdx.x; q < n; q += kReorderThreads)
+                d[q] = s[q];
+        }
     }
 }
 
