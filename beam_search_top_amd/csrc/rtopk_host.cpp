@@ -67,8 +67,10 @@ int pow2_ceil(int x)
     return p;
 }
 
-// Validates the scalar arguments and computes the decomposition.
-int make_plan(const void *logits, int B, int beam, int V, int k, int dtype, rtopk::Plan *p)
+// Validates the scalar arguments and computes the decomposition. With G
+// vocabulary shards each row is G shard rows of V / G logits: pieces are cut
+// per shard row (cps of them) and a row has chunks = G * cps pieces.
+int make_plan(const void *logits, int B, int beam, int V, int k, int dtype, rtopk::Plan *p, int G = 1)
 {
     if (dtype != RTOPK_F32 && dtype != RTOPK_F16 && dtype != RTOPK_BF16)
         return fail(RTOPK_EINVAL, "unknown dtype %d", dtype);
@@ -89,10 +91,12 @@ int make_plan(const void *logits, int B, int beam, int V, int k, int dtype, rtop
     if (mis % p->elem_bytes)
         return fail(RTOPK_EINVAL, "logits pointer is not aligned to its element size");
     p->align_elems = (int)(mis / p->elem_bytes);
-    const bool aligned_rows = p->align_elems == 0 && V % p->epv == 0;
-    // 16-byte vectors one row touches at most
-    const long long span = aligned_rows ? V / p->epv : ceil_div(V, p->epv) + 1;
+    const int Vs = V / G; // logits of one shard row
+    const bool aligned_rows = p->align_elems == 0 && Vs % p->epv == 0;
+    // 16-byte vectors one shard row touches at most
+    const long long span = aligned_rows ? Vs / p->epv : ceil_div(Vs, p->epv) + 1;
     const long long rows = (long long)B * beam;
+    const long long srows = rows * G; // shard rows
 
     int nv = g_override_nv.load();
     long long C;
@@ -102,8 +106,8 @@ int make_plan(const void *logits, int B, int beam, int V, int k, int dtype, rtop
         const int nvmax = max_vecs_per_thread(aligned_rows);
         const long long c0 = ceil_div(span, (long long)rtopk::kLanes * nvmax);
         C = c0;
-        if (rows * c0 < kTargetGrid) {
-            long long want = ceil_div(kTargetGrid, rows);
+        if (srows * c0 < kTargetGrid) {
+            long long want = ceil_div(kTargetGrid, srows);
             // no smaller than kMinVecs vectors per lane: past that, more pieces
             // add per-piece overhead faster than they add memory parallelism
             long long cmax = ceil_div(span, (long long)rtopk::kLanes * kMinVecs);
@@ -123,14 +127,14 @@ int make_plan(const void *logits, int B, int beam, int V, int k, int dtype, rtop
         // the workgroup: its rows are then selected inside it (row-local),
         // which saves a cross-workgroup round trip per piece; at most half of
         // the pieces are given up for it.
-        if (g_rowlocal.load() && waves_for(rows * C) % C != 0) {
+        if (g_rowlocal.load() && waves_for(srows * C) % (G * C) != 0) {
             for (int v : kVecsPerThread) {
                 if (v <= nv || v > nvmax)
                     continue;
                 const long long c2 = ceil_div(span, (long long)rtopk::kLanes * v);
                 if (2 * c2 < C)
                     break;
-                if (waves_for(rows * c2) % c2 == 0) {
+                if (waves_for(srows * c2) % (G * c2) == 0) {
                     nv = v;
                     C = c2;
                     break;
@@ -139,6 +143,10 @@ int make_plan(const void *logits, int B, int beam, int V, int k, int dtype, rtop
         }
     }
     p->vecs_per_thread = nv;
+    p->nshards = G;
+    p->vshard = Vs;
+    p->cps = (int)C;
+    C *= G; // pieces per row
     p->chunks = (int)C;
     // pieces hold exactly lanes*nv vectors (so the kernel's unmasked path
     // covers them), except a row's last piece, which holds the remainder
@@ -217,10 +225,16 @@ struct Debug {
 
 int enqueue(const rtopk::Plan &p, const void *logits, int dtype, const float *alive,
             const uint8_t *finished, int B, int beam, int V, int k, int eos_id, int32_t *ob,
-            int32_t *ot, float *os, void *ws, const Debug &dbg, hipStream_t stream)
+            int32_t *ot, float *os, void *ws, const Debug &dbg, hipStream_t stream,
+            const void *const *shards = nullptr)
 {
     rtopk::StepArgs a{};
     a.logits_aligned = (const uint8_t *)logits - (size_t)p.align_elems * p.elem_bytes;
+    a.vshard = p.vshard;
+    a.cps = p.cps;
+    a.ms = rtopk::make_magic((uint32_t)p.cps);
+    for (int g = 0; g < rtopk::kMaxShards; ++g)
+        a.shard[g] = shards && g < p.nshards ? (const uint8_t *)shards[g] : a.logits_aligned;
     a.alive = alive;
     a.finished = finished;
     a.B = B;
@@ -328,6 +342,44 @@ int rtopk_beam_step(const void *logits, int dtype, const float *alive_scores,
         return st;
     return enqueue(p, logits, dtype, alive_scores, finished_mask, B, beam, V, k, eos_id, out_beam_ids,
                    out_token_ids, out_scores, ws, Debug{}, (hipStream_t)stream);
+}
+
+int rtopk_beam_step_sharded(const void *const *shards, int nshards, int dtype, const float *alive_scores,
+                            const uint8_t *finished_mask, int B, int beam, int V_shard, int k, int eos_id,
+                            int32_t *out_beam_ids, int32_t *out_token_ids, float *out_scores, void *stream)
+{
+    if (!shards)
+        return fail(RTOPK_EINVAL, "shards is NULL");
+    if (nshards < 1 || nshards > rtopk::kMaxShards)
+        return fail(RTOPK_EINVAL, "nshards=%d outside [1, %d]", nshards, rtopk::kMaxShards);
+    for (int g = 0; g < nshards; ++g) {
+        if (!shards[g])
+            return fail(RTOPK_EINVAL, "shard %d is NULL", g);
+        if ((uintptr_t)shards[g] % 16)
+            return fail(RTOPK_EINVAL, "shard %d is not 16-byte aligned", g);
+    }
+    int st = check_pointers(shards[0], alive_scores, out_beam_ids, out_token_ids, out_scores);
+    if (st != RTOPK_OK)
+        return st;
+    if (V_shard < 1)
+        return fail(RTOPK_EINVAL, "V_shard=%d must be >= 1", V_shard);
+    const int esz = dtype == RTOPK_F32 ? 4 : 2;
+    if ((long long)V_shard * esz % 16)
+        return fail(RTOPK_EINVAL, "V_shard=%d: a shard row of %lld bytes is not a multiple of 16", V_shard,
+                    (long long)V_shard * esz);
+    if ((long long)V_shard * nshards > INT_MAX)
+        return fail(RTOPK_EINVAL, "V_shard*nshards exceeds 2^31-1");
+    const int V = V_shard * nshards;
+    rtopk::Plan p;
+    if ((st = make_plan(shards[0], B, beam, V, k, dtype, &p, nshards)) != RTOPK_OK)
+        return st;
+    if (eos_id < 0 || eos_id >= V)
+        return fail(RTOPK_EINVAL, "eos_id=%d outside [0, %d)", eos_id, V);
+    void *ws = nullptr;
+    if ((st = acquire_workspace(p.ws_bytes, (hipStream_t)stream, &ws)) != RTOPK_OK)
+        return st;
+    return enqueue(p, shards[0], dtype, alive_scores, finished_mask, B, beam, V, k, eos_id, out_beam_ids,
+                   out_token_ids, out_scores, ws, Debug{}, (hipStream_t)stream, shards);
 }
 
 size_t rtopk_workspace_bytes(int B, int beam, int V, int k, int dtype)

@@ -14,7 +14,8 @@ constexpr int kMaxChunkLimit = 64;  // candidates a piece stages in LDS (one per
 constexpr int kMaxSortKeys = 512;   // LDS sort keys of the per-batch selection
 constexpr int kMaxPieces = 3072;    // pieces (beam * chunks) of one batch element (LDS tables)
 constexpr int kMaxK = 64;
-constexpr int kTicketCap = 65536;   // batch elements the ticket region holds (B limit)
+constexpr int kTicketCap = 65536;
+constexpr int kMaxShards = 8;       // vocabulary shards of one sharded call   // batch elements the ticket region holds (B limit)
 
 // Division by a launch constant d >= 1 for dividends n < 2^31:
 // floor(n / d) = (n * mul) >> shr with shr = 31 + ceil(log2 d) and
@@ -50,6 +51,12 @@ struct StepArgs {
     int rowlocal;                  // workgroups hold whole rows (chunks divides waves)
     int maxl;                      // row-local: workgroup lists per batch element, at most
     Magic mc, mb, mp, mw;          // division by chunks, beam, beam*chunks, waves
+    // Vocabulary shards: a row's pieces g*cps .. g*cps + cps - 1 lie in shard g,
+    // whose [B][beam][vshard] tensor starts at shard[g] (one shard: shard[0] is
+    // logits_aligned, vshard = V, cps = chunks). Token t of shard g is g*vshard + t.
+    int vshard, cps;
+    Magic ms;                      // division by cps
+    const uint8_t *shard[kMaxShards];
     // workspace; only the ticket region must be zero when a call starts
     uint32_t *ticket;              // [kTicketCap] arrivals, first B used
     uint64_t *head;                // [B*beam*chunks][2]: (max2 | sum << 32), (threshold | count << 32)
@@ -69,6 +76,7 @@ struct Plan {
     int elem_bytes, epv;
     int chunks, vecs_per_thread, vecs_per_chunk;
     int ngroups, chunk_limit, queue_cap, align_elems, sort_keys, waves, rowlocal, maxl;
+    int nshards, vshard, cps; // vocabulary shards, logits per shard row, pieces per shard row
     long long grid;
     size_t lds_bytes;
     size_t ws_ticket_off, ws_head_off, ws_slots_off, ws_bytes;

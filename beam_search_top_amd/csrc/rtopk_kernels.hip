@@ -525,20 +525,24 @@ __device__ __forceinline__ void select_piece(const StepArgs &a, SelectLds &sm, u
     // multiplication: the loads issue after a few instructions.
     const uint32_t uu = valid ? u : row0 * (uint32_t)a.chunks;
     const uint32_t row = mdiv(uu, a.mc);
-    const int c = (int)(uu - row * (uint32_t)a.chunks);
+    const int cr = (int)(uu - row * (uint32_t)a.chunks); // piece of the row
+    const int g = (int)mdiv((uint32_t)cr, a.ms);          // its vocabulary shard
+    const int c = cr - g * a.cps;                         // piece of the shard's row
     const int j = (int)(row - mdiv(row, a.mb) * (uint32_t)a.beam);
     // this row's shared group maxima (rows are counted from the workgroup's first)
     uint32_t *gshare = gshare_rows + (row - row0) * kMaxK;
     // Vectors are counted in the 16-byte-aligned frame of the tensor; a row
     // starts `lead` elements into its first vector v0 and spans `span` vectors.
     // Everything per lane is 32-bit and relative to the row.
-    const uint64_t e0 = (uint64_t)row * (uint32_t)a.V + (uint32_t)a.align_elems;
+    const int VS = a.vshard; // logits of this row in its shard (V when unsharded)
+    const uint64_t e0 = (uint64_t)row * (uint32_t)VS + (uint32_t)a.align_elems;
     const uint64_t v0 = e0 / EPV;
     const int lead = (int)(e0 - v0 * EPV);
-    const int span = (lead + a.V + EPV - 1) / EPV;
+    const int span = (lead + VS + EPV - 1) / EPV;
     const int pbeg = c * a.vecs_per_chunk; // piece start, vectors from v0
     const int pend = pbeg + a.vecs_per_chunk < span ? pbeg + a.vecs_per_chunk : span;
-    const uint32_t flat0 = (uint32_t)j * (uint32_t)a.V - (uint32_t)lead; // flat index of slot 0 of vector 0
+    // flat index j*V + vocabulary index of slot 0 of vector 0
+    const uint32_t flat0 = (uint32_t)j * (uint32_t)a.V + (uint32_t)g * (uint32_t)VS - (uint32_t)lead;
 
     // The finished flag is loaded first but tested only once the piece's
     // loads are in flight: its latency under a full memory system overlaps
@@ -562,7 +566,7 @@ __device__ __forceinline__ void select_piece(const StepArgs &a, SelectLds &sm, u
     // lines the end of the step needs.
     const uint32_t nbytes = valid && pend > pbeg ? (uint32_t)(pend - pbeg) * 16u : 0u;
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t *>(a.logits_aligned) + (v0 + (uint64_t)pbeg) * 16u, 0, nbytes, 0x00020000);
+        const_cast<uint8_t *>(a.shard[g]) + (v0 + (uint64_t)pbeg) * 16u, 0, nbytes, 0x00020000);
     uint4 d[NV];
 #pragma unroll
     for (int r = 0; r < NV; ++r) {
@@ -611,7 +615,7 @@ __device__ __forceinline__ void select_piece(const StepArgs &a, SelectLds &sm, u
 #pragma unroll
                 for (int i = 0; i < EPV; ++i) {
                     const int t = q * EPV + i - lead;
-                    Tr::mask_if(d[r], i, q >= pend || t < 0 || t >= a.V);
+                    Tr::mask_if(d[r], i, q >= pend || t < 0 || t >= VS);
                 }
             }
             Tr::update(acc, d[r]);
@@ -755,7 +759,7 @@ __device__ __forceinline__ void select_piece(const StepArgs &a, SelectLds &sm, u
                     for (int i = 0; i < EPV; ++i) {
                         const float x = Tr::elem(d[r], i);
                         const int t = q * EPV + i - lead;
-                        const bool h = x >= T && inq && (MODE != kGeneral || (t >= 0 && t < a.V));
+                        const bool h = x >= T && inq && (MODE != kGeneral || (t >= 0 && t < VS));
                         const uint64_t m = ballot(h);
                         if (m != 0) {
                             const uint32_t pos = wn + lane_prefix(m);
@@ -783,7 +787,7 @@ __device__ __forceinline__ void select_piece(const StepArgs &a, SelectLds &sm, u
         auto valid = [&](int r, int i) {
             const int q = qb0 + r * kLanes;
             const int t = q * EPV + i - lead;
-            return q < pend && (MODE != kGeneral || (t >= 0 && t < a.V));
+            return q < pend && (MODE != kGeneral || (t >= 0 && t < VS));
         };
         float prev = INFINITY, v = -INFINITY;
         uint32_t above = 0;
@@ -1874,7 +1878,7 @@ hipError_t launch_dtype<RTOPK_DTYPE>(const StepArgs &a, int nv, size_t lds, hipS
     constexpr int DT = RTOPK_DTYPE;
     const long long pieces = (long long)a.B * a.beam * a.chunks;
     const dim3 grid((unsigned)((pieces + a.waves - 1) / a.waves)), block(kLanes * a.waves);
-    const bool aligned = a.align_elems == 0 && a.V % Traits<DT>::epv == 0;
+    const bool aligned = a.align_elems == 0 && a.vshard % Traits<DT>::epv == 0;
     const bool rl = a.rowlocal != 0;
     switch (nv) {
 #define RTOPK_CASE(N)                                                                      \

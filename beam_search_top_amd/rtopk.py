@@ -67,6 +67,9 @@ def load():
     L.rtopk_set_override.restype = i32
     L.rtopk_set_row_local.argtypes = [i32]
     L.rtopk_set_row_local.restype = i32
+    L.rtopk_beam_step_sharded.argtypes = [ctypes.POINTER(vp), i32, i32, vp, vp, i32, i32, i32, i32, i32,
+                                          vp, vp, vp, vp]
+    L.rtopk_beam_step_sharded.restype = i32
     L.rtopk_beam_reorder.argtypes = [vp, vp, ctypes.c_longlong, i32, i32, ctypes.c_longlong, vp, i32, vp]
     L.rtopk_beam_reorder.restype = i32
     L.rtopk_read_probe.argtypes = [vp, sz, ctypes.c_uint32, vp, vp]
@@ -124,6 +127,33 @@ def rtopk_set_override(vecs_per_thread, chunk_limit):
 
 def rtopk_set_row_local(enable):
     return load().rtopk_set_row_local(enable)
+
+
+def rtopk_beam_step_sharded(shards, dtype, alive_scores, finished_mask, B, beam, V_shard, k, eos_id,
+                            out_beam_ids, out_token_ids, out_scores, stream):
+    """`shards` is a Python sequence of device addresses (marshalled into the host array)."""
+    arr = (ctypes.c_void_p * len(shards))(*shards) if shards is not None else None
+    return load().rtopk_beam_step_sharded(arr, len(shards) if shards is not None else 0, dtype, alive_scores,
+                                          finished_mask, B, beam, V_shard, k, eos_id, out_beam_ids,
+                                          out_token_ids, out_scores, stream)
+
+
+def beam_step_sharded(shards, alive, finished=None, k=None, eos_id=2):
+    """One selection step over vocabulary shards (torch device tensors
+    [B, beam, V_shard] of one dtype, shard g holding vocabulary indices
+    g*V_shard ...), on the current stream. Returns (beam_ids, token_ids, scores)."""
+    import torch
+    s0 = shards[0]
+    if any(t.shape != s0.shape or t.dtype != s0.dtype or not t.is_contiguous() for t in shards):
+        raise ValueError("shards must be contiguous tensors of one shape and dtype")
+    if k is None:
+        k = s0.shape[1]
+    B, beam, Vs = s0.shape
+    _, _, _, finished, outs = _prepare(s0, alive, finished, k)
+    stream = torch.cuda.current_stream(s0.device).cuda_stream
+    _check(rtopk_beam_step_sharded([_ptr(t) for t in shards], dtype_code(s0), _ptr(alive), _ptr(finished),
+                                   B, beam, Vs, k, eos_id, _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]), stream))
+    return outs
 
 
 def rtopk_beam_reorder(src, dst, nslabs, B, beam, row_bytes, beam_ids, ld, stream):

@@ -15,6 +15,7 @@ host cores as a baseline.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config b128]
 """
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -196,6 +197,8 @@ def main():
     ap.add_argument("--steps", type=int, default=5000)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--config", default="b128")
+    ap.add_argument("--shards", type=int, default=1,
+                    help="select over G vocabulary shards (rtopk_beam_step_sharded), each its own tensor")
     ap.add_argument("--path", default="select", choices=["select", "reorder"],
                     help="select: the selection step (the default line); reorder: the cache refresh after it")
     ap.add_argument("--launch", default="graph", choices=["graph", "eager"],
@@ -237,6 +240,11 @@ def main():
     fin = torch.from_numpy(s.finished).to(dev)
     nbuf = max(1, math.ceil(args.pool_mib * 2**20 / s.logit_bytes))
     pool = [x0] + [torch.roll(x0, shifts=7919 * i, dims=2).contiguous() for i in range(1, nbuf)]
+    G = args.shards
+    if G > 1:  # each pool entry becomes G shard tensors [B, beam, V/G]
+        Vs = s.V // G
+        pool = [[x[:, :, g * Vs:(g + 1) * Vs].contiguous() for g in range(G)] for x in pool]
+        shard_arrays = [(ctypes.c_void_p * G)(*[t.data_ptr() for t in shards]) for shards in pool]
     ob = torch.empty((s.B, s.k), dtype=torch.int32, device=dev)
     ot = torch.empty((s.B, s.k), dtype=torch.int32, device=dev)
     osc = torch.empty((s.B, s.k), dtype=torch.float32, device=dev)
@@ -247,11 +255,16 @@ def main():
     L = rtopk.load()
     fixed = (s.dtype, alive.data_ptr(), fin.data_ptr(), s.B, s.beam, s.V, s.k, s.eos_id,
              ob.data_ptr(), ot.data_ptr(), osc.data_ptr())
-    ptrs = [p.data_ptr() for p in pool]
+    ptrs = [p.data_ptr() for p in pool] if G == 1 else [shards[0].data_ptr() for shards in pool]
     wsp = ws.data_ptr()
 
     def launch(i, stream):
-        rc = L.rtopk_beam_step_ws(ptrs[i % nbuf], *fixed, wsp, nws, stream)
+        if G == 1:
+            rc = L.rtopk_beam_step_ws(ptrs[i % nbuf], *fixed, wsp, nws, stream)
+        else:
+            rc = L.rtopk_beam_step_sharded(shard_arrays[i % nbuf], G, s.dtype, alive.data_ptr(), fin.data_ptr(),
+                                           s.B, s.beam, s.V // G, s.k, s.eos_id, ob.data_ptr(), ot.data_ptr(),
+                                           osc.data_ptr(), stream)
         if rc != 0:
             raise RuntimeError(rtopk.rtopk_last_error())
 
@@ -269,6 +282,9 @@ def main():
         graph = torch.cuda.CUDAGraph()
         cs = torch.cuda.Stream()
         cs.wait_stream(cur)
+        if G > 1:  # the sharded entry point uses the library workspace of its stream: create it before capture
+            launch(0, cs.cuda_stream)
+            torch.cuda.synchronize()
         with torch.cuda.graph(graph, stream=cs):
             for i in range(glen):
                 launch(i, torch.cuda.current_stream().cuda_stream)
@@ -313,7 +329,8 @@ def main():
         torch.cuda.synchronize()
 
     alg = algorithmic_bytes(s)
-    ceiling = None if args.no_read_ceiling else read_ceiling(L, ptrs, alg, K, cur)
+    # the probe reads alg contiguous bytes of one buffer: only an unsharded pool has them
+    ceiling = None if args.no_read_ceiling or G > 1 else read_ceiling(L, ptrs, alg, K, cur)
     traffic = read_traffic(args.config)  # measured HBM bytes per launch, if taken on these sources
     achieved = alg / (ms_step * 1e-3) / 1e9
     cpu = None
@@ -336,7 +353,7 @@ def main():
         "config": {
             "workload": f"{s.name}: B={s.B} beam={s.beam} k={s.k} V={s.V} {dtype_name} logits, "
                         f"{s.n_finished}/{s.B * s.beam} beams finished, seed {s.seed}",
-            "B": s.B, "beam": s.beam, "k": s.k, "V": s.V, "launch": args.launch,
+            "B": s.B, "beam": s.beam, "k": s.k, "V": s.V, "launch": args.launch, "vocab_shards": G,
             "logit_pool_buffers": nbuf, "chunks": plan.chunks, "vecs_per_thread": plan.vecs_per_thread,
             "grid": plan.grid,
         },

@@ -128,6 +128,26 @@ int rtopk_beam_step(const void *logits, int dtype, const float *alive_scores,
                     int32_t *out_beam_ids, int32_t *out_token_ids, float *out_scores,
                     void *stream);
 
+/*
+ * rtopk_beam_step on a vocabulary split into nshards shards, as a
+ * vocabulary-parallel LM head leaves it: shard g is its own device tensor
+ * [B][beam][V_shard] holding vocabulary indices g*V_shard .. (g+1)*V_shard - 1.
+ * Each shard row is processed on its own (its pieces' R-top-k thresholds, exact
+ * per-piece candidates and log-sum-exp partials) and only those are merged per
+ * beam and batch element -- the exchange a multi-GPU vocabulary split needs
+ * (the article's rough-select kernel and candidate queue, applied per shard),
+ * here inside one launch on one GPU. Results equal rtopk_beam_step on the
+ * concatenated [B][beam][nshards*V_shard] logits (token ids are vocabulary
+ * indices), up to the fp32 rounding of the log-sum-exp merge order.
+ *   shards    HOST array of nshards device pointers, each 16-byte aligned
+ *   nshards   1..8
+ *   V_shard   logits per shard row; V_shard * element size must be a multiple of 16
+ * Everything else as rtopk_beam_step (library-owned workspace, eos_id < nshards*V_shard).
+ */
+int rtopk_beam_step_sharded(const void *const *shards, int nshards, int dtype, const float *alive_scores,
+                            const uint8_t *finished_mask, int B, int beam, int V_shard, int k, int eos_id,
+                            int32_t *out_beam_ids, int32_t *out_token_ids, float *out_scores, void *stream);
+
 /* Bytes of caller workspace rtopk_beam_step_ws needs for this shape (0 on bad arguments). */
 size_t rtopk_workspace_bytes(int B, int beam, int V, int k, int dtype);
 

@@ -162,3 +162,19 @@ def test_read_probe_validation(lib):
     assert rtopk.rtopk_read_probe(None, 64, 0, 0x2000, None) == rtopk.RTOPK_EINVAL
     assert rtopk.rtopk_read_probe(0x1000, 64, 0, None, None) == rtopk.RTOPK_EINVAL
     assert "read probe" in rtopk.rtopk_last_error()
+
+
+@pytest.mark.parametrize("shards,nshards_override,Vs,eos,msg", [
+    (None, None, 8, 0, "shards is NULL"),
+    ([0x1000] * 9, None, 8, 0, "nshards"),
+    ([0x1000, 0], None, 8, 0, "shard 1 is NULL"),
+    ([0x1000, 0x2008], None, 8, 0, "not 16-byte aligned"),
+    ([0x1000, 0x2000], None, 5, 0, "multiple of 16"),
+    ([0x1000, 0x2000], None, 8, 16, "eos_id"),
+    ([0x1000, 0x2000], None, 0, 0, "V_shard"),
+])
+def test_sharded_validation_rejects_before_launch(lib, shards, nshards_override, Vs, eos, msg):
+    st = rtopk.rtopk_beam_step_sharded(shards, rtopk.RTOPK_F16, 0x3000, None, 2, 2, Vs, 2, eos,
+                                       0x4000, 0x5000, 0x6000, None)
+    assert st == rtopk.RTOPK_EINVAL, rtopk.rtopk_last_error()
+    assert msg in rtopk.rtopk_last_error()
