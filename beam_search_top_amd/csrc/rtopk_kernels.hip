@@ -1170,8 +1170,9 @@ __device__ __forceinline__ void sort_batch(const StepArgs &a, const SortLds &sm,
         a.out_token[o] = (int32_t)(flat - jj * (uint32_t)a.V);
         a.out_score[o] = from_ord((uint32_t)(key >> 32));
     };
-    if (ns <= (uint32_t)nth) {
+    if (ns <= (uint32_t)nth && ns <= K) {
         // rank counting: keys are distinct (flat indices are), so ranks are a permutation
+        // (only keys that fit the LDS were staged: more survivors take the argmax rounds)
         if ((uint32_t)tid < ns) {
             const uint64_t mine = sm.keys[tid];
             uint32_t rank = 0;

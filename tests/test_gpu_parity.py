@@ -273,3 +273,19 @@ def test_candidate_scoring_exactly_at_the_bound():
     check(s, got)
     ref = oracle.step_of(s)
     assert got[1][105, 3] == ref.token_ids[105, 3]
+
+
+@pytest.mark.parametrize("B,beam,k,V,dt,dist", [
+    (32, 1, 64, 50000, synth.BF16, "gumbel"), (16, 2, 64, 40000, synth.F16, "int"),
+    (8, 1, 48, 100000, synth.BF16, "gumbel"),
+])
+def test_more_survivors_than_lds_keys(B, beam, k, V, dt, dist):
+    # regression: a batch element whose survivors outnumber the LDS sort keys
+    # (512) but not the workgroup's threads must take the argmax rounds, not
+    # rank the first 512 and read past them
+    s = synth.make_custom(B, beam, k, V, dt, seed=B * 31 + k, dist=dist, sigma=1.0)
+    st, p = rtopk.rtopk_plan(None, s.B, s.beam, s.V, s.k, s.dtype)
+    assert st == 0
+    print(f"[parity] {s.name} row_local={p.row_local} sort_keys={p.sort_keys} threads={p.pieces_per_group * 64}",
+          flush=True)
+    check(s, run(s))
