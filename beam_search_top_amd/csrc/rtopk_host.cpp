@@ -13,6 +13,7 @@
 
 #include <atomic>
 #include <climits>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <map>
@@ -321,6 +322,39 @@ int acquire_workspace(size_t need, hipStream_t stream, void **out)
     return RTOPK_OK;
 }
 
+// A device buffer of zeros per device (the running scores of sampling rows),
+// zero-filled once and never written after; grown when a call needs more.
+std::map<int, WsEntry> g_zeros;
+
+int acquire_zeros(size_t n, hipStream_t stream, const float **out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return fail(RTOPK_EHIP, "hipGetDevice failed");
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    WsEntry &z = g_zeros[dev];
+    const size_t bytes = n * sizeof(float);
+    if (z.bytes < bytes) {
+        const size_t grow = bytes > 2 * z.bytes ? bytes : 2 * z.bytes;
+        void *p = nullptr;
+        hipError_t e = hipMalloc(&p, grow);
+        if (e != hipSuccess)
+            return fail(RTOPK_ENOMEM, "hipMalloc(%zu) for the zero scores: %s", grow, hipGetErrorString(e));
+        if ((e = rtopk::launch_zero(p, grow, stream)) != hipSuccess || (e = hipStreamSynchronize(stream)) != hipSuccess) {
+            (void)hipFree(p);
+            return fail(RTOPK_EHIP, "zero-filling the zero scores: %s", hipGetErrorString(e));
+        }
+        if (z.ptr) { // an earlier, smaller buffer may still be read by enqueued work
+            (void)hipDeviceSynchronize();
+            (void)hipFree(z.ptr);
+        }
+        z.ptr = p;
+        z.bytes = grow;
+    }
+    *out = (const float *)z.ptr;
+    return RTOPK_OK;
+}
+
 } // namespace
 
 extern "C" {
@@ -484,6 +518,41 @@ int rtopk_set_row_local(int enable)
     return RTOPK_OK;
 }
 
+int rtopk_sample_step(const void *logits, int dtype, int R, int V, int k, float temperature, uint64_t seed,
+                      uint64_t step, int32_t *out_token, float *out_logprob, void *stream)
+{
+    if (!logits || !out_token || !out_logprob)
+        return fail(RTOPK_EINVAL, "sample step: NULL pointer");
+    if (!(temperature > 0.f) || !std::isfinite(temperature))
+        return fail(RTOPK_EINVAL, "sample step: temperature must be finite and > 0");
+    rtopk::Plan p;
+    int st = make_plan(logits, R, 1, V, k, dtype, &p);
+    if (st != RTOPK_OK)
+        return st;
+    // the selection's outputs follow its workspace; a zero running score per row
+    const size_t off = align256(p.ws_bytes);
+    const size_t rk = (size_t)R * (size_t)k;
+    const size_t need = off + 3 * align256(4 * rk);
+    void *ws = nullptr;
+    if ((st = acquire_workspace(need, (hipStream_t)stream, &ws)) != RTOPK_OK)
+        return st;
+    const float *zeros = nullptr;
+    if ((st = acquire_zeros((size_t)R, (hipStream_t)stream, &zeros)) != RTOPK_OK)
+        return st;
+    uint8_t *w = (uint8_t *)ws;
+    int32_t *ob = (int32_t *)(w + off);
+    int32_t *ot = (int32_t *)(w + off + align256(4 * rk));
+    float *os = (float *)(w + off + 2 * align256(4 * rk));
+    if ((st = enqueue(p, logits, dtype, zeros, nullptr, R, 1, V, k, 0, ob, ot, os, ws, Debug{},
+                      (hipStream_t)stream)) != RTOPK_OK)
+        return st;
+    const hipError_t e = rtopk::launch_topk_sample(ot, os, R, k, temperature, seed, step, out_token, out_logprob,
+                                                   (hipStream_t)stream);
+    if (e != hipSuccess)
+        return fail(RTOPK_EHIP, "sample launch: %s", hipGetErrorString(e));
+    return RTOPK_OK;
+}
+
 int rtopk_beam_reorder(const void *src, void *dst, long long nslabs, int B, int beam, long long row_bytes,
                        const int32_t *beam_ids, int ld, void *stream)
 {
@@ -539,6 +608,14 @@ void rtopk_release(void)
         }
     }
     g_ws.clear();
+    for (auto &kv : g_zeros) {
+        if (kv.second.ptr) {
+            (void)hipSetDevice(kv.first);
+            (void)hipDeviceSynchronize();
+            (void)hipFree(kv.second.ptr);
+        }
+    }
+    g_zeros.clear();
     if (cur >= 0)
         (void)hipSetDevice(cur);
 }

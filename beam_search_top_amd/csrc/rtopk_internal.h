@@ -89,6 +89,9 @@ hipError_t launch_dtype(const StepArgs &a, int vecs_per_thread, size_t lds_bytes
 
 // Enqueue a zero fill of `bytes` (multiple of 4) at `p` (no hipMemsetAsync).
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream);
+// top-k sampling (rtopk_sample.hip)
+hipError_t launch_topk_sample(const int32_t *tok, const float *sc, int R, int k, float tau, uint64_t seed,
+                              uint64_t step, int32_t *out_tok, float *out_lp, hipStream_t stream);
 // cache refresh (rtopk_reorder.hip)
 long long reorder_chunk_bytes();
 hipError_t launch_beam_reorder(const void *src, void *dst, long long nslabs, int B, int beam, long long row_bytes,

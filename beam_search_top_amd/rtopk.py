@@ -70,6 +70,9 @@ def load():
     L.rtopk_beam_step_sharded.argtypes = [ctypes.POINTER(vp), i32, i32, vp, vp, i32, i32, i32, i32, i32,
                                           vp, vp, vp, vp]
     L.rtopk_beam_step_sharded.restype = i32
+    L.rtopk_sample_step.argtypes = [vp, i32, i32, i32, i32, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64,
+                                    vp, vp, vp]
+    L.rtopk_sample_step.restype = i32
     L.rtopk_beam_reorder.argtypes = [vp, vp, ctypes.c_longlong, i32, i32, ctypes.c_longlong, vp, i32, vp]
     L.rtopk_beam_reorder.restype = i32
     L.rtopk_read_probe.argtypes = [vp, sz, ctypes.c_uint32, vp, vp]
@@ -154,6 +157,26 @@ def beam_step_sharded(shards, alive, finished=None, k=None, eos_id=2):
     _check(rtopk_beam_step_sharded([_ptr(t) for t in shards], dtype_code(s0), _ptr(alive), _ptr(finished),
                                    B, beam, Vs, k, eos_id, _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]), stream))
     return outs
+
+
+def rtopk_sample_step(logits, dtype, R, V, k, temperature, seed, step, out_token, out_logprob, stream):
+    return load().rtopk_sample_step(logits, dtype, R, V, k, temperature, seed, step, out_token, out_logprob,
+                                    stream)
+
+
+def sample_step(logits, k, temperature=1.0, seed=0, step=0):
+    """Top-k sampling of every row of logits [R, V] (torch device tensor) on
+    the current stream. Returns (tokens [R] int32, logprobs [R] float32)."""
+    import torch
+    if logits.dim() != 2 or not logits.is_contiguous() or not logits.is_cuda:
+        raise ValueError("logits must be a contiguous [R, V] device tensor")
+    R, V = logits.shape
+    tok = torch.empty(R, dtype=torch.int32, device=logits.device)
+    lp = torch.empty(R, dtype=torch.float32, device=logits.device)
+    stream = torch.cuda.current_stream(logits.device).cuda_stream
+    _check(rtopk_sample_step(_ptr(logits), dtype_code(logits), R, V, k, float(temperature), int(seed), int(step),
+                             _ptr(tok), _ptr(lp), stream))
+    return tok, lp
 
 
 def rtopk_beam_reorder(src, dst, nslabs, B, beam, row_bytes, beam_ids, ld, stream):

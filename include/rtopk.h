@@ -209,6 +209,28 @@ int rtopk_set_override(int vecs_per_thread, int chunk_limit);
 int rtopk_set_row_local(int enable);
 
 /*
+ * Top-k sampling with the same hierarchical selection. The LightSeq inference
+ * article reports sampling-decode speedups next to its beam-search ones (its
+ * results passage). Every row r < R of logits [R][V] is selected as a batch
+ * element with one beam and a zero running score, which gives its k best
+ * tokens with scores s_i = x_i - lse(row), best first (ties: lower token).
+ * One of them is then drawn from the top-k distribution at `temperature`:
+ *     w_i = exp((s_i - s_1) / temperature),   S = w_1 + ... + w_k (rank order, fp32),
+ *     u   = (word 0 of Philox4x64-10 with counter (r, step, 0, 0) and key
+ *            (seed, 0)) >> 40, times 2^-24,
+ *     i   = the first rank with u*S < w_1 + ... + w_i (the last rank if none).
+ *   out_token    device [R] int32: the token of rank i
+ *   out_logprob  device [R] float32: log(w_i / S), its log-probability under the
+ *                top-k distribution
+ * 1 <= k <= min(64, V); temperature finite and > 0. The same (seed, step) draws
+ * the same tokens. Uses the library-owned workspace of `stream` (allocated on
+ * the first call for a shape, like rtopk_beam_step) and a library-owned buffer
+ * of zero scores per device.
+ */
+int rtopk_sample_step(const void *logits, int dtype, int R, int V, int k, float temperature, uint64_t seed,
+                      uint64_t step, int32_t *out_token, float *out_logprob, void *stream);
+
+/*
  * Cache refresh after a selection step. The LightSeq inference article's
  * hierarchical-decoding passage ends the step with a cache update once the
  * top-k are known (its profile: 10% of latency in fp32, 6% in fp16). For a

@@ -161,3 +161,77 @@ def beam_reorder(src, dst_before, beam_ids, nslabs, B, beam):
             if 0 <= i < beam:
                 out[:, b, j, :] = src[:, b, i, :]
     return out.reshape(nslabs, B * beam, -1)
+
+
+# Philox4x64-10 (Salmon, Moraes, Dror, Shaw, SC 2011), from its definition:
+# round constants, Weyl key increments, ten rounds.
+_PH_M0, _PH_M1 = 0xD2E7470EE14C6C93, 0xCA5A826395121157
+_PH_W0, _PH_W1 = 0x9E3779B97F4A7C15, 0xBB67AE8584CAA73B
+_M64 = (1 << 64) - 1
+
+
+def philox4x64(counter, key, rounds=10):
+    """The four 64-bit words of Philox4x64 for a 4-word counter and 2-word key."""
+    c0, c1, c2, c3 = (int(v) & _M64 for v in counter)
+    k0, k1 = (int(v) & _M64 for v in key)
+    for _ in range(rounds):
+        p0, p1 = _PH_M0 * c0, _PH_M1 * c2
+        c0, c1, c2, c3 = ((p1 >> 64) ^ c1 ^ k0), p1 & _M64, ((p0 >> 64) ^ c3 ^ k1), p0 & _M64
+        k0, k1 = (k0 + _PH_W0) & _M64, (k1 + _PH_W1) & _M64
+    return c0, c1, c2, c3
+
+
+def sample_uniform(seed, row, step):
+    """u in [0, 1): the 24 high bits of word 0 of Philox4x64-10 with counter
+    (row, step, 0, 0) and key (seed, 0), times 2^-24 (exact in float32)."""
+    return np.float32((philox4x64((row, step, 0, 0), (seed, 0))[0] >> 40) * 2.0 ** -24)
+
+
+class Sample:
+    """Oracle output of top-k sampling: tokens [R], log-probabilities [R]
+    (float64), and each row's decision margin |u*S - C_j| / S at the nearest
+    cumulative sum boundary (float32 decisions within a few ulps of a boundary
+    may go either way in another implementation)."""
+
+    def __init__(self, tokens, logprobs, margins, topk_tokens):
+        self.tokens, self.logprobs, self.margins, self.topk_tokens = tokens, logprobs, margins, topk_tokens
+
+
+def sample_from_list(topk_tokens, topk_scores, temperature, seed, draw) -> Sample:
+    """The draw of top-k sampling from given per-row lists (tokens and float32
+    scores, best first): weights w_i = exp((s_i - s_1) / temperature) and
+    their running sums in rank order in float32, one Philox uniform per row
+    (counter (row, draw)), the first rank whose running sum exceeds u * S
+    (the last if none)."""
+    toks_in = np.asarray(topk_tokens)
+    sc = np.asarray(topk_scores, dtype=np.float32)
+    R, k = sc.shape
+    toks = np.empty(R, np.int32)
+    lps = np.empty(R, np.float64)
+    margins = np.empty(R, np.float64)
+    tau = np.float32(temperature)
+    for r in range(R):
+        s = sc[r]
+        w = [np.float32(np.exp(np.float32(np.float32(s[i] - s[0]) / tau))) for i in range(k)]
+        c, acc = [], np.float32(0.0)
+        for wi in w:
+            acc = np.float32(acc + wi)
+            c.append(acc)
+        S = acc
+        u = sample_uniform(seed, r, draw)
+        t = np.float32(u * S)
+        i = next((j for j in range(k) if t < c[j]), k - 1)
+        toks[r] = toks_in[r, i]
+        lps[r] = float(np.log(np.float64(w[i]) / np.float64(S)))
+        margins[r] = min(abs(float(t) - float(cj)) for cj in c) / float(S)
+    return Sample(toks, lps, margins, toks_in)
+
+
+def sample(logits, dtype, k, temperature, seed, draw) -> Sample:
+    """Top-k sampling by its definition: every row's exact top-k (the oracle's
+    full log-softmax and full sort, with one beam and a zero running score),
+    then the draw of sample_from_list on those lists."""
+    x = _logits(logits, dtype)
+    R, V = x.shape
+    res = step(x.reshape(R, 1, V), dtype, np.zeros((R, 1), np.float32), None, k, eos_id=0)
+    return sample_from_list(res.token_ids, res.scores, temperature, seed, draw)
