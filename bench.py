@@ -175,6 +175,67 @@ def bench_reorder(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_sample(args):
+    """Top-k sampling decode (rtopk_sample_step): R = 512 rows (sequences) of
+    V = 40000 fp16 logits ~ N(0, 3), k = 40, temperature 1, one Philox draw
+    per row; rows rotate through a 1 GiB pool so every step reads cold HBM.
+    Algorithmic bytes = every logit once + the [R] token and log-prob outputs."""
+    import numpy as np
+    import torch
+
+    from beam_search_top_amd import rtopk
+    L = rtopk.load()
+    dev = torch.device("cuda:0")
+    R, V, k = 512, 40000, 40
+    rng = np.random.default_rng(1008)
+    x0 = torch.from_numpy(rng.normal(0, 3.0, size=(R, V)).astype(np.float16)).to(dev)
+    nbuf = max(1, math.ceil(args.pool_mib * 2**20 / (R * V * 2)))
+    pool = [x0] + [torch.roll(x0, shifts=7919 * i, dims=1).contiguous() for i in range(1, nbuf)]
+    tok = torch.empty(R, dtype=torch.int32, device=dev)
+    lp = torch.empty(R, dtype=torch.float32, device=dev)
+    cur = torch.cuda.current_stream()
+
+    def launch(i, stream):
+        rc = L.rtopk_sample_step(pool[i % nbuf].data_ptr(), 1, R, V, k, 1.0, 77, i, tok.data_ptr(), lp.data_ptr(),
+                                 stream)
+        if rc != 0:
+            raise RuntimeError(rtopk.rtopk_last_error())
+
+    for i in range(max(2, args.warmup)):
+        launch(i, cur.cuda_stream)
+    graph = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(cur)
+    launch(0, cs.cuda_stream)  # the library workspace of the capture stream exists before capture
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=cs):
+        for i in range(100):
+            launch(i, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    reps = max(1, args.steps // 100)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(cur)
+    for _ in range(reps):
+        graph.replay()
+    end.record(cur)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / (reps * 100)
+    alg = R * V * 2 + 8 * R
+    gbps = alg / (ms * 1e-3) / 1e9
+    line = {
+        "metric": "top-k sampling decode steps/sec and logit GB/s (% HBM peak), 1xMI355X",
+        "value": 1e3 / ms, "unit": "sample-steps/s", "n_gpus": 1, "steps": reps * 100, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"sample_r512: R={R} rows x V={V} fp16 N(0,3), k={k}, temperature 1, seed 1008",
+                   "R": R, "V": V, "k": k, "logit_pool_buffers": nbuf},
+        "algorithmic_bytes_per_step": alg,
+        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": None},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def cpu_baseline(s, seconds):
     import oracle
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
@@ -199,8 +260,9 @@ def main():
     ap.add_argument("--config", default="b128")
     ap.add_argument("--shards", type=int, default=1,
                     help="select over G vocabulary shards (rtopk_beam_step_sharded), each its own tensor")
-    ap.add_argument("--path", default="select", choices=["select", "reorder"],
-                    help="select: the selection step (the default line); reorder: the cache refresh after it")
+    ap.add_argument("--path", default="select", choices=["select", "reorder", "sample"],
+                    help="select: the selection step (the default line); reorder: the cache refresh after it; "
+                         "sample: top-k sampling with the same selection")
     ap.add_argument("--launch", default="graph", choices=["graph", "eager"],
                     help="replay the K launches from a captured HIP graph, or launch each from Python")
     ap.add_argument("--pool-mib", type=int, default=1024, help="distinct logit buffers rotated through")
@@ -217,6 +279,9 @@ def main():
 
     if args.path == "reorder":
         bench_reorder(args)
+        return
+    if args.path == "sample":
+        bench_sample(args)
         return
 
     import numpy as np
