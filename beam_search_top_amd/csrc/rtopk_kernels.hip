@@ -251,6 +251,27 @@ __device__ __forceinline__ float wave_sum_f(float v)
     v = v + dpp_f<0x140>(v);
     return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
 }
+template <int CTRL> __device__ __forceinline__ uint32_t dpp_u(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    v = max(v, dpp_u<0xb1>(v));
+    v = max(v, dpp_u<0x4e>(v));
+    v = max(v, dpp_u<0x141>(v));
+    v = max(v, dpp_u<0x140>(v));
+    return max(max((uint32_t)__builtin_amdgcn_readlane(v, 0), (uint32_t)__builtin_amdgcn_readlane(v, 16)),
+               max((uint32_t)__builtin_amdgcn_readlane(v, 32), (uint32_t)__builtin_amdgcn_readlane(v, 48)));
+}
+// Wave maximum of 64-bit keys with DPP only: the largest high word, then the
+// largest low word among the lanes that hold it. Every lane must be active.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t v)
+{
+    const uint32_t hi = wave_max_u32((uint32_t)(v >> 32));
+    const uint32_t lo = wave_max_u32((uint32_t)(v >> 32) == hi ? (uint32_t)v : 0u);
+    return ((uint64_t)hi << 32) | lo;
+}
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
 {
 #pragma unroll
@@ -1495,6 +1516,26 @@ __device__ __forceinline__ uint32_t wave_topk(uint64_t *keys, uint32_t n, int k,
             if (rank < (uint32_t)k)
                 best_out[rank] = mine;
         }
+    } else if (n <= 8u * kLanes) {
+        // up to 8 keys per lane, held in registers; k rounds of a DPP wave
+        // maximum of the keys below the previous round's (keys are distinct)
+        uint64_t mine[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t i = (uint32_t)lane + (uint32_t)j * kLanes;
+            mine[j] = i < n ? keys[i] : 0ull;
+        }
+        uint64_t prev = ~0ull;
+        for (uint32_t round = 0; round < kept; ++round) {
+            uint64_t best = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                best = mine[j] < prev && mine[j] > best ? mine[j] : best;
+            best = wave_max_key(best);
+            if (lane == 0)
+                best_out[round] = best;
+            prev = best;
+        }
     } else {
         uint64_t prev = ~0ull;
         for (uint32_t round = 0; round < kept; ++round) {
@@ -1503,7 +1544,7 @@ __device__ __forceinline__ uint32_t wave_topk(uint64_t *keys, uint32_t n, int k,
                 const uint64_t x = keys[i];
                 best = x < prev && x > best ? x : best;
             }
-            best = wave_max_u64(best);
+            best = wave_max_key(best);
             if (lane == 0)
                 best_out[round] = best;
             prev = best;
