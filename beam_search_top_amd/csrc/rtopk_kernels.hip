@@ -715,14 +715,17 @@ __device__ __forceinline__ void select_piece(const StepArgs &a, SelectLds &sm, u
     float T;
     if (ng == a.k) { // the R-top-k: the least group maximum
         T = wave_min_f(cur);
-    } else { // k below a power of two: the k-th largest of the ngroups maxima
-        int gt = 0, ge = 0;
-        for (int e = 0; e < ng; ++e) {
-            const float w = lane_f(cur, e);
-            gt += w > cur;
-            ge += w >= cur;
+    } else { // k below a power of two: the k-th largest of the ngroups maxima,
+        // the largest t (order-preserving bits) that at least k of them reach,
+        // found bit by bit from the top with one compare and ballot per bit
+        const uint32_t o = lane < ng ? ord_bits(cur) : 0u;
+        uint32_t t = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t c = t | (1u << bit);
+            if (__builtin_popcountll(ballot(o >= c)) >= a.k)
+                t = c;
         }
-        T = wave_max_f(lane < ng && gt < a.k && a.k <= ge ? cur : -INFINITY);
+        T = from_ord(t);
     }
 
     // ---- pass 2: stage the sort key of every valid logit >= T. The wave
