@@ -18,7 +18,7 @@
 //    never waits for another wave after its loads are issued, and the only
 //    cross-lane traffic is DPP, readlane and ballots inside the wave. A
 //    workgroup holds `waves` consecutive pieces: 16 when the whole grid is
-//    resident at once, 4 when workgroups run in rounds (a workgroup frees its
+//    resident at once, 8 when workgroups run in rounds (a workgroup frees its
 //    CU only when its slowest wave is done).
 //  * Pass 1 keeps one running maximum per element slot (packed v_pk_max_f16
 //    for fp16) and accumulates the log-sum-exp online in fp32, base 2,
