@@ -274,7 +274,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the selection step of a batch "
-              "element needs no other GPU, and this build measures the one-GPU kernel.", file=sys.stderr)
+              "element needs no other GPU, and the benchmark measures the one-GPU kernel.", file=sys.stderr)
         sys.exit(2)
 
     if args.path == "reorder":
