@@ -39,16 +39,24 @@
 //  * Cross-workgroup data moves only through device-coherent (sc1) atomic
 //    stores and loads, so no L2 writeback or invalidate is ever needed.
 //    Device-scope atomics on one address serialise at the memory side, so
-//    arrivals are counted in two levels: the waves of a workgroup count
-//    themselves in LDS, and the last of them adds the workgroup's piece count
-//    to the ticket of each batch element it touched (two arrivals per ticket
-//    for 4 x 40000-logit batch elements). The wave that completes a ticket
-//    merges the pieces' (max, sum) partials by a fixed tree, applies the
-//    per-beam threshold max_c T_c and the batch bound
-//    S = max_j (alive_j + T_j - lse_j) (at least k candidates score >= S),
-//    and selects the k best survivors. It then puts the ticket back to zero;
-//    tickets live in a region of the workspace that no shape uses for
-//    anything else.
+//    they are issued per workgroup and batch element, never per wave.
+//  * Row-local workgroups (a row's pieces divide the workgroup, e.g. 4 x
+//    40000-logit fp16 batch elements: 8 pieces per row, 2 rows per
+//    workgroup) keep every piece's results in LDS and select their rows
+//    there: merge each row's (max, sum) partials by DPP butterflies, apply
+//    the row threshold max_c T_c and the bound S = max_j (alive_j + T_j -
+//    lse_j) (at least k candidates score >= S), keep the k best. The
+//    workgroups sharing a batch element count their arrival at its ticket
+//    before selecting (low 16 bits); all but the last publish their k keys
+//    and then count the publication (high 16 bits); the last waits for those
+//    counts, merges the lists and writes the outputs.
+//  * Other workgroups publish each piece's top-k and partials; wave 0 adds
+//    the workgroup's piece count to the ticket of each batch element it
+//    touched, and the workgroup that completes a ticket merges every piece
+//    of that batch element in the same way.
+//  * A ticket is put back to zero by the workgroup that finishes its batch
+//    element; tickets live in a region of the workspace that no shape uses
+//    for anything else.
 // Compiled once per logit type (-DRTOPK_DTYPE=0 float32, 1 float16,
 // 2 bfloat16) so the instantiations build in parallel; the float32 unit also
 // holds the type-independent host helpers.
