@@ -178,3 +178,16 @@ def test_sharded_validation_rejects_before_launch(lib, shards, nshards_override,
                                        0x4000, 0x5000, 0x6000, None)
     assert st == rtopk.RTOPK_EINVAL, rtopk.rtopk_last_error()
     assert msg in rtopk.rtopk_last_error()
+
+
+def test_planner_workgroup_rules(lib):
+    # grids that run in rounds (more pieces than 16 per CU on 256 CUs) use 8-wave workgroups
+    st, p = rtopk.rtopk_plan(None, 64, 8, 250000, 8, 2)
+    assert st == 0 and 64 * 8 * p.chunks > 4096 and p.pieces_per_group == 8  # B*beam*chunks pieces
+    # with k >= 16, a row-local workgroup holds one batch element instead of several
+    st, p = rtopk.rtopk_plan(None, 512, 1, 40000, 40, 1)
+    assert st == 0 and p.row_local == 1 and p.pieces_per_group == p.chunks == 8
+    st, p = rtopk.rtopk_plan(None, 512, 1, 40000, 8, 1)  # small k keeps 16-piece workgroups
+    assert st == 0 and p.row_local == 1 and p.pieces_per_group == 16
+    st, p = rtopk.rtopk_plan(None, 128, 4, 40000, 4, 1)  # the 4 x 40000 fp16 shape: 2 rows per workgroup
+    assert st == 0 and p.row_local == 1 and p.chunks == 8 and p.pieces_per_group == 16 and p.grid == 256
