@@ -10,7 +10,7 @@ namespace rtopk {
 
 constexpr int kLanes = 64;          // one wave64 per piece
 constexpr int kMaxWaves = 16;       // pieces (waves) per workgroup, at most
-constexpr int kMaxChunkLimit = 64;  // candidates a piece stages in LDS (one per lane)
+constexpr int kMaxChunkLimit = 128; // candidates a piece stages in LDS (up to two per lane)
 constexpr int kMaxSortKeys = 512;   // LDS sort keys of the per-batch selection
 constexpr int kMaxPieces = 3072;    // pieces (beam * chunks) of one batch element (LDS tables)
 constexpr int kMaxK = 64;

@@ -533,7 +533,7 @@ __device__ __forceinline__ uint32_t *ticket_of(const StepArgs &a, int b)
 
 // in row-local workgroups also the piece's published top-k and header.
 struct SelectLds {
-    uint64_t stage[kLanes];
+    uint64_t stage[2 * kLanes]; // a piece's staged candidates (up to kMaxChunkLimit)
     uint64_t top[kMaxK];
     float hm, hs, ht; // lse partial (max2, sum) and threshold
     uint32_t hemit;   // keys in top
@@ -898,23 +898,40 @@ __device__ __forceinline__ void select_piece(const StepArgs &a, SelectLds &sm, u
     // element's top-k. Keys are distinct, so ranks are unique.
     uint64_t *mine = a.slots + (long long)u * a.k;
     const uint32_t emit = nst < (uint32_t)a.k ? nst : (uint32_t)a.k;
-    uint64_t key = 0;
-    uint32_t rank = ~0u;
+    // up to two staged keys per lane (lane, lane + 64), ranked among all nst
+    uint64_t key = 0, key2 = 0;
+    uint32_t rank = ~0u, rank2 = ~0u;
     if ((uint32_t)lane < nst) {
         key = sm.stage[lane];
         rank = lane;
-        if (nst > (uint32_t)a.k) {
-            rank = 0;
+    }
+    if ((uint32_t)lane + kLanes < nst) {
+        key2 = sm.stage[lane + kLanes];
+        rank2 = lane + kLanes;
+    }
+    if (nst > (uint32_t)kLanes) { // uniform: the second half of the stage is in use
+        uint32_t r1 = 0, r2 = 0;
 #pragma unroll 8
-            for (uint32_t i = 0; i < nst; ++i)
-                rank += sm.stage[i] > key;
+        for (uint32_t i = 0; i < nst; ++i) {
+            const uint64_t x = sm.stage[i];
+            r1 += x > key;
+            r2 += x > key2;
         }
+        rank = (uint32_t)lane < nst ? r1 : ~0u;
+        rank2 = (uint32_t)lane + kLanes < nst ? r2 : ~0u;
+    } else if (nst > (uint32_t)a.k && (uint32_t)lane < nst) {
+        rank = 0;
+#pragma unroll 8
+        for (uint32_t i = 0; i < nst; ++i)
+            rank += sm.stage[i] > key;
     }
     if (RL) {
         // The workgroup holds whole rows and selects them itself: the piece's
         // top-k and header stay in LDS; nothing to store or drain.
         if (rank < (uint32_t)a.k)
             sm.top[rank] = key;
+        if (rank2 < (uint32_t)a.k)
+            sm.top[rank2] = key2;
         if (lane == 0) {
             sm.hm = pm;
             sm.hs = ps;
@@ -927,17 +944,27 @@ __device__ __forceinline__ void select_piece(const StepArgs &a, SelectLds &sm, u
             if (a.dbg_hits)
                 a.dbg_hits[u] = wn;
         }
-        if (a.dbg_count && rank < (uint32_t)a.k) { // debug: append to the batch element's queue
+        if (a.dbg_count) { // debug: append to the batch element's queue
             const int b = row / a.beam;
-            const uint32_t pos = atomicAdd(&a.dbg_count[b], 1u);
-            if (a.dbg_queue)
-                a.dbg_queue[(long long)b * a.queue_cap + pos] =
-                    ((uint64_t)__float_as_uint(entry_x(key)) << 32) | entry_flat(key);
+            if (rank < (uint32_t)a.k) {
+                const uint32_t pos = atomicAdd(&a.dbg_count[b], 1u);
+                if (a.dbg_queue)
+                    a.dbg_queue[(long long)b * a.queue_cap + pos] =
+                        ((uint64_t)__float_as_uint(entry_x(key)) << 32) | entry_flat(key);
+            }
+            if (rank2 < (uint32_t)a.k) {
+                const uint32_t pos = atomicAdd(&a.dbg_count[b], 1u);
+                if (a.dbg_queue)
+                    a.dbg_queue[(long long)b * a.queue_cap + pos] =
+                        ((uint64_t)__float_as_uint(entry_x(key2)) << 32) | entry_flat(key2);
+            }
         }
         return;
     }
     if (rank < (uint32_t)a.k)
         put64(&mine[rank], key);
+    if (rank2 < (uint32_t)a.k)
+        put64(&mine[rank2], key2);
     if (lane == 0) {
         put64(&a.head[2 * (long long)u], ((uint64_t)__float_as_uint(ps) << 32) | __float_as_uint(pm));
         put64(&a.head[2 * (long long)u + 1], ((uint64_t)emit << 32) | __float_as_uint(T));

@@ -158,8 +158,12 @@ def make_step(name: str, seed: int | None = None) -> Step:
 
 
 def make_custom(B, beam, k, V, dtype, seed, dist="normal", sigma=1.0, alive_lo=-10.0,
-                n_finished=0, const=None) -> Step:
-    """A free-shape step for edge cases: normal / uniform / gumbel / constant rows."""
+                n_finished=0, const=None, top_ties=0) -> Step:
+    """A free-shape step for edge cases: normal / uniform / gumbel / constant rows.
+
+    top_ties > 0 sets that many random positions of every row to one value
+    (64.0, exact in every logit type) above all the other draws: the row's
+    top logit then repeats top_ties times, ties broken by flat index."""
     rng = np.random.default_rng(seed)
     if const is not None:
         x = np.full((B, beam, V), const, np.float64)
@@ -173,8 +177,12 @@ def make_custom(B, beam, k, V, dtype, seed, dist="normal", sigma=1.0, alive_lo=-
         x = rng.integers(-3, 4, (B, beam, V)).astype(np.float64)
     else:
         raise ValueError(dist)
+    if top_ties:
+        for row in x.reshape(B * beam, V):
+            row[rng.choice(V, size=min(top_ties, V), replace=False)] = 64.0
     alive = rng.uniform(alive_lo, 0.0, (B, beam))
     fin = _finished_mask(rng, B, beam, n_finished)
-    return Step(name=f"custom_{B}x{beam}x{V}_k{k}_{DTYPE_NAMES[dtype]}_{dist}", B=B, beam=beam, k=k,
+    tag = f"_ties{top_ties}" if top_ties else ""
+    return Step(name=f"custom_{B}x{beam}x{V}_k{k}_{DTYPE_NAMES[dtype]}_{dist}{tag}", B=B, beam=beam, k=k,
                 V=V, dtype=dtype, logits=to_dtype(x, dtype),
                 alive=np.ascontiguousarray(alive, dtype=np.float32), finished=fin, seed=seed)

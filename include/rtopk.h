@@ -194,7 +194,7 @@ int rtopk_plan(const void *logits, int B, int beam, int V, int k, int dtype, rto
  * Process-wide tuning overrides for experiments and tests (0 = automatic):
  * vecs_per_thread forces the 16-byte vectors each thread holds (one of
  * 1,2,3,4,6,8,10,12; others are rejected with RTOPK_EINVAL);
- * chunk_limit forces the per-piece LDS candidate limit (1..64, raised to k),
+ * chunk_limit forces the per-piece LDS candidate limit (1..128, raised to k),
  * which makes the argmax-rounds top-k path run whenever a piece has more
  * candidates.
  */

@@ -126,7 +126,7 @@ def test_plan_covers_rows(lib, shape):
 def test_overrides(lib):
     try:
         assert rtopk.rtopk_set_override(5, 0) == rtopk.RTOPK_EINVAL
-        assert rtopk.rtopk_set_override(0, 65) == rtopk.RTOPK_EINVAL
+        assert rtopk.rtopk_set_override(0, 129) == rtopk.RTOPK_EINVAL
         assert rtopk.rtopk_set_override(0, -1) == rtopk.RTOPK_EINVAL
         assert rtopk.rtopk_set_override(4, 1) == 0
         st, p = rtopk.rtopk_plan(None, 4, 4, 40000, 4, 1)
@@ -135,7 +135,7 @@ def test_overrides(lib):
     finally:
         rtopk.rtopk_set_override(0, 0)
     st, p = rtopk.rtopk_plan(None, 4, 4, 40000, 4, 1)
-    assert p.chunk_limit == 64
+    assert p.chunk_limit == 128
 
 
 def test_row_local_switch(lib):

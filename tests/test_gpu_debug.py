@@ -137,3 +137,12 @@ def test_intermediates_overflow():
     finally:
         rtopk.rtopk_set_override(0, 0)
     assert check_intermediates(s, d, align) > 0  # some pieces took the exact top-k path
+
+
+def test_intermediates_two_keys_per_lane():
+    s = synth.make_custom(2, 4, 8, 40000, synth.F16, seed=11, top_ties=768)
+    d, align = run_debug(s)
+    h = np.asarray(d["hits"])
+    wide = int(((h > 64) & (h <= d["plan"]["chunk_limit"])).sum())
+    assert wide > 0  # pieces that used the second half of the stage
+    assert check_intermediates(s, d, align) == 0

@@ -289,3 +289,15 @@ def test_more_survivors_than_lds_keys(B, beam, k, V, dt, dist):
     print(f"[parity] {s.name} row_local={p.row_local} sort_keys={p.sort_keys} threads={p.pieces_per_group * 64}",
           flush=True)
     check(s, run(s))
+
+
+@pytest.mark.parametrize("B,beam,k,V,dt,ties", [
+    (2, 4, 8, 40000, synth.F16, 768),      # ~96 tied top logits per piece, row-local path
+    (2, 4, 64, 40000, synth.F32, 1536),    # k = 64 drawn from ~96 ties per piece
+    (2, 8, 8, 250000, synth.BF16, 5952),   # per-piece publication path
+])
+def test_more_hits_than_lanes(B, beam, k, V, dt, ties):
+    # pieces with 65..128 hits stage two keys per lane and rank both halves
+    s = synth.make_custom(B, beam, k, V, dt, seed=ties + k, top_ties=ties)
+    print(f"[parity] {s.name}", flush=True)
+    check(s, run(s))
