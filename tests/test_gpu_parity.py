@@ -301,3 +301,20 @@ def test_more_hits_than_lanes(B, beam, k, V, dt, ties):
     s = synth.make_custom(B, beam, k, V, dt, seed=ties + k, top_ties=ties)
     print(f"[parity] {s.name}", flush=True)
     check(s, run(s))
+
+
+@pytest.mark.parametrize("B,beam,k,V,dt,kw", [
+    (2, 8, 8, 250000, synth.BF16, dict(const=1.0)),                  # every slot survives: 3968 keys
+    (3, 8, 8, 250000, synth.BF16, dict(const=1.0, n_finished=2)),    # ... and finished beams offer their end token
+    (2, 8, 4, 250000, synth.F16, dict(dist="int")),                  # heavy ties across beams
+    (2, 8, 16, 250000, synth.BF16, dict(const=0.5)),                 # 7936 slots
+])
+def test_survivors_past_lds_keys_small_k(B, beam, k, V, dt, kw):
+    # the per-batch selection with more survivors than its LDS keys and a
+    # small k: the argmax rounds over every published slot, with ties
+    s = synth.make_custom(B, beam, k, V, dt, seed=k + beam, **kw)
+    st, p = rtopk.rtopk_plan(None, s.B, s.beam, s.V, s.k, s.dtype)
+    assert st == 0 and not p.row_local
+    print(f"[parity] {s.name} slots/batch={beam * p.chunks * k} sort_keys={p.sort_keys} "
+          f"threads={p.pieces_per_group * 64}", flush=True)
+    check(s, run(s))
