@@ -756,7 +756,7 @@ __device__ __forceinline__ void select_piece(const StepArgs &a, SelectLds &sm, u
         // (independent) compares first; the others, whose tail already fills
         // the registers, test each vector as they go
         uint64_t vm[NV];
-        if constexpr (RL) {
+        if constexpr (RL > 0) {
 #pragma unroll
             for (int r = 0; r < NV; ++r) {
                 opaque(d[r]);
@@ -1538,9 +1538,61 @@ __device__ __forceinline__ void sort_batch_wave(const StepArgs &a, const SortLds
 // top-k restricted to one workgroup's rows lies in that workgroup's list, so
 // the last list to arrive merges exactly: one round trip of a few keys.
 
+// The kept (<= 64) best of keys[0..n), 64 < n <= 512, into best_out by rank:
+// up to 8 keys per lane, held in registers. t, the kept-th largest key, by a
+// search over its bits from the top: a candidate prefix stays when at least
+// `kept` keys are >= it (one ballot per register and bit), and the search
+// stops once exactly `kept` keys are >= t (keys are distinct). Those are
+// compacted to keys[0..kept) and ranked by counting.
+__device__ __forceinline__ void wave_topk_bits(uint64_t *keys, uint32_t n, uint32_t kept, int lane, uint64_t *best_out)
+{
+    uint64_t mine[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t i = (uint32_t)lane + (uint32_t)j * kLanes;
+        mine[j] = i < n ? keys[i] : 0ull; // 0: below every real key
+    }
+    uint64_t t = 0;
+    uint32_t cnt_t = n;
+    for (int bit = 63; bit >= 0 && cnt_t != kept; --bit) { // uniform
+        const uint64_t c = t | (1ull << bit);
+        uint32_t cnt = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            cnt += (uint32_t)__builtin_popcountll(ballot(mine[j] >= c));
+        if (cnt >= kept) {
+            t = c;
+            cnt_t = cnt;
+        }
+    }
+    wave_sync(); // every lane has read keys[] before it is rewritten
+    uint32_t pos = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const bool sel = (uint32_t)lane + (uint32_t)j * kLanes < n && mine[j] >= t;
+        const uint64_t m = ballot(sel);
+        const uint32_t q = pos + lane_prefix(m);
+        if (sel && q < kept)
+            keys[q] = mine[j];
+        pos += (uint32_t)__builtin_popcountll(m);
+    }
+    wave_sync();
+    if ((uint32_t)lane < kept) { // kept <= k <= 64
+        const uint64_t x = keys[lane];
+        uint32_t rank = 0;
+#pragma unroll 8
+        for (uint32_t i = 0; i < kept; ++i)
+            rank += keys[i] > x;
+        best_out[rank] = x;
+    }
+}
+
 // Keys of this workgroup's selection: the k best of keys[0..n), then either
 // the outputs or the published list. `rank` of lane entries by counting when
-// n <= 64, else k rounds of wave argmax. Returns the number kept.
+// n <= 64; up to 512 keys, a search for the k-th largest key's bits in the
+// kernels built for k > 8 (BIGK), else k rounds of wave argmax; more, k rounds
+// over LDS. Returns the number kept; keys[] may be overwritten.
+template <bool BIGK>
 __device__ __forceinline__ uint32_t wave_topk(uint64_t *keys, uint32_t n, int k, int lane, uint64_t *best_out)
 {
     const uint32_t kept = n < (uint32_t)k ? n : (uint32_t)k;
@@ -1554,6 +1606,8 @@ __device__ __forceinline__ uint32_t wave_topk(uint64_t *keys, uint32_t n, int k,
             if (rank < (uint32_t)k)
                 best_out[rank] = mine;
         }
+    } else if (BIGK && n <= 8u * kLanes) {
+        wave_topk_bits(keys, n, kept, lane, best_out);
     } else if (n <= 8u * kLanes) {
         // up to 8 keys per lane, held in registers; k rounds of a DPP wave
         // maximum of the keys below the previous round's (keys are distinct)
@@ -1616,6 +1670,7 @@ __device__ __forceinline__ void emit_outputs(const StepArgs &a, int b, const uin
 // Returns the number of keys of this workgroup's list (in `best`) and sets
 // `done` when this workgroup arrived last among those holding rows of b and
 // every other list is published; the caller then runs row_merge.
+template <bool BIGK>
 __device__ __forceinline__ uint32_t row_select(const StepArgs &a, const SelectLds *wl, uint64_t *keys, uint64_t *best,
                                            uint32_t ufirst, int LG, int b, int j0, int j1, int lane,
                                            bool &done)
@@ -1683,7 +1738,7 @@ __device__ __forceinline__ uint32_t row_select(const StepArgs &a, const SelectLd
         offer(ok, ok ? score_key(alv, (uint32_t)j * (uint32_t)a.V + (uint32_t)a.eos_id) : 0ull);
     }
     wave_sync();
-    const uint32_t kept = wave_topk(keys, ns, k, lane, best);
+    const uint32_t kept = wave_topk<BIGK>(keys, ns, k, lane, best);
 
     done = false;
     if (whole) { // every row of b is here
@@ -1723,6 +1778,7 @@ __device__ __forceinline__ uint32_t row_select(const StepArgs &a, const SelectLd
 
 // The last workgroup of batch element b to arrive merges its own list (in
 // LDS, `best`, `kept` keys) with the lists every other workgroup published.
+template <bool BIGK>
 __device__ __forceinline__ void row_merge(const StepArgs &a, uint64_t *keys, uint64_t *best, uint32_t kept,
                                           int b, int LG, int lane)
 {
@@ -1748,7 +1804,7 @@ __device__ __forceinline__ void row_merge(const StepArgs &a, uint64_t *keys, uin
         n += (uint32_t)__builtin_popcountll(mk);
     }
     wave_sync();
-    const uint32_t nk = wave_topk(keys, n, k, lane, best);
+    const uint32_t nk = wave_topk<BIGK>(keys, n, k, lane, best);
     emit_outputs(a, b, best, nk, lane);
     if (lane == 0)
         put32(ticket_of(a, b), 0u);
@@ -1819,7 +1875,7 @@ __device__ __forceinline__ void rtopk_step_tail(const StepArgs &a, GroupLds &g, 
 
 // RL: row-local workgroups (chunks divides waves), a separate instantiation so
 // that neither tail's register needs weigh on the other.
-template <int DT, int NV, bool ALIGNED, bool RL>
+template <int DT, int NV, bool ALIGNED, int RL> // RL: 0 per-piece publication, 1 row-local, 2 row-local, k > 8
 __global__ __launch_bounds__(kLanes *kMaxWaves) void rtopk_step(const StepArgs a)
 {
     extern __shared__ __align__(16) uint8_t lds[];
@@ -1840,7 +1896,7 @@ __global__ __launch_bounds__(kLanes *kMaxWaves) void rtopk_step(const StepArgs a
     for (int i = tid; i < W * kMaxK; i += kLanes * W)
         gshare[i] = 0x007fffffu; // ord_bits(-inf)
     lds_barrier();
-    select_piece<DT, NV, ALIGNED ? kAligned : kGeneral, RL>(
+    select_piece<DT, NV, ALIGNED ? kAligned : kGeneral, (RL > 0)>(
         a, *reinterpret_cast<SelectLds *>(lds + hdr + wave * sizeof(SelectLds)), gshare, u, u < total, row0, lane);
 
     // Every wave has drained its stores. A workgroup's resources are released
@@ -1849,7 +1905,7 @@ __global__ __launch_bounds__(kLanes *kMaxWaves) void rtopk_step(const StepArgs a
     // elements, and the workgroup selects the outputs of any it completed.
     lds_barrier();
     const uint32_t ulast = (ufirst + W < total ? ufirst + W : total) - 1;
-    if constexpr (RL) {
+    if constexpr (RL > 0) {
         if (wave != 0)
             return;
         const SelectLds *wl = reinterpret_cast<const SelectLds *>(lds + hdr);
@@ -1861,9 +1917,9 @@ __global__ __launch_bounds__(kLanes *kMaxWaves) void rtopk_step(const StepArgs a
             const int j0 = rfirst > b * a.beam ? rfirst - b * a.beam : 0;
             const int j1 = rlast < (b + 1) * a.beam - 1 ? rlast - b * a.beam : a.beam - 1;
             bool done;
-            const uint32_t kept = row_select(a, wl, keys, best, ufirst, LG, b, j0, j1, lane, done);
+            const uint32_t kept = row_select<(RL > 1)>(a, wl, keys, best, ufirst, LG, b, j0, j1, lane, done);
             if (done)
-                row_merge(a, keys, best, kept, b, LG, lane);
+                row_merge<(RL > 1)>(a, keys, best, kept, b, LG, lane);
             wave_sync();
         }
     } else {
@@ -1959,18 +2015,22 @@ hipError_t launch_dtype<RTOPK_DTYPE>(const StepArgs &a, int nv, size_t lds, hipS
     const long long pieces = (long long)a.B * a.beam * a.chunks;
     const dim3 grid((unsigned)((pieces + a.waves - 1) / a.waves)), block(kLanes * a.waves);
     const bool aligned = a.align_elems == 0 && a.vshard % Traits<DT>::epv == 0;
-    const bool rl = a.rowlocal != 0;
+    const int rl = a.rowlocal == 0 ? 0 : a.k > 8 ? 2 : 1;
     switch (nv) {
 #define RTOPK_CASE(N)                                                                      \
     case N:                                                                                \
-        if (aligned && rl)                                                                 \
-            hipLaunchKernelGGL((rtopk_step<DT, N, true, true>), grid, block, lds, s, a);   \
+        if (aligned && rl == 2)                                                            \
+            hipLaunchKernelGGL((rtopk_step<DT, N, true, 2>), grid, block, lds, s, a);      \
+        else if (aligned && rl == 1)                                                       \
+            hipLaunchKernelGGL((rtopk_step<DT, N, true, 1>), grid, block, lds, s, a);      \
         else if (aligned)                                                                  \
-            hipLaunchKernelGGL((rtopk_step<DT, N, true, false>), grid, block, lds, s, a);  \
-        else if (rl)                                                                       \
-            hipLaunchKernelGGL((rtopk_step<DT, N, false, true>), grid, block, lds, s, a);  \
+            hipLaunchKernelGGL((rtopk_step<DT, N, true, 0>), grid, block, lds, s, a);      \
+        else if (rl == 2)                                                                  \
+            hipLaunchKernelGGL((rtopk_step<DT, N, false, 2>), grid, block, lds, s, a);     \
+        else if (rl == 1)                                                                  \
+            hipLaunchKernelGGL((rtopk_step<DT, N, false, 1>), grid, block, lds, s, a);     \
         else                                                                               \
-            hipLaunchKernelGGL((rtopk_step<DT, N, false, false>), grid, block, lds, s, a); \
+            hipLaunchKernelGGL((rtopk_step<DT, N, false, 0>), grid, block, lds, s, a);     \
         break;
         RTOPK_CASE(1) RTOPK_CASE(2) RTOPK_CASE(3) RTOPK_CASE(4) RTOPK_CASE(6) RTOPK_CASE(8)
         RTOPK_CASE(10) RTOPK_CASE(12)
