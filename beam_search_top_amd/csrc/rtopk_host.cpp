@@ -232,10 +232,20 @@ struct Debug {
     uint64_t *queue = nullptr;
 };
 
+struct SampleArgs { // a top-k draw fused into the selection (row-local kernels built for k > 8)
+    int32_t *token = nullptr;
+    float *logprob = nullptr;
+    float tau = 1.f;
+    uint64_t seed = 0, step = 0;
+};
+
+// Whether the selection kernel of this plan draws the sample itself.
+bool fused_draw(const rtopk::Plan &p, int k) { return p.rowlocal != 0 && k > 8; }
+
 int enqueue(const rtopk::Plan &p, const void *logits, int dtype, const float *alive,
             const uint8_t *finished, int B, int beam, int V, int k, int eos_id, int32_t *ob,
             int32_t *ot, float *os, void *ws, const Debug &dbg, hipStream_t stream,
-            const void *const *shards = nullptr)
+            const void *const *shards = nullptr, const SampleArgs &smp = SampleArgs{})
 {
     rtopk::StepArgs a{};
     a.logits_aligned = (const uint8_t *)logits - (size_t)p.align_elems * p.elem_bytes;
@@ -272,6 +282,11 @@ int enqueue(const rtopk::Plan &p, const void *logits, int dtype, const float *al
     a.out_beam = ob;
     a.out_token = ot;
     a.out_score = os;
+    a.smp_token = smp.token;
+    a.smp_logprob = smp.logprob;
+    a.smp_tau = smp.tau;
+    a.smp_seed = smp.seed;
+    a.smp_step = smp.step;
     a.dbg_T = dbg.T;
     a.dbg_hits = dbg.hits;
     a.dbg_lse = dbg.lse;
@@ -551,9 +566,22 @@ int rtopk_sample_step(const void *logits, int dtype, int R, int V, int k, float 
     int32_t *ob = (int32_t *)(w + off);
     int32_t *ot = (int32_t *)(w + off + align256(4 * rk));
     float *os = (float *)(w + off + 2 * align256(4 * rk));
+    // row-local kernels built for k > 8 draw right after each row's top-k;
+    // the others leave the lists to the draw kernel
+    SampleArgs smp;
+    const bool fused = fused_draw(p, k);
+    if (fused) {
+        smp.token = out_token;
+        smp.logprob = out_logprob;
+        smp.tau = temperature;
+        smp.seed = seed;
+        smp.step = step;
+    }
     if ((st = enqueue(p, logits, dtype, zeros, nullptr, R, 1, V, k, 0, ob, ot, os, ws, Debug{},
-                      (hipStream_t)stream)) != RTOPK_OK)
+                      (hipStream_t)stream, nullptr, smp)) != RTOPK_OK)
         return st;
+    if (fused)
+        return RTOPK_OK;
     const hipError_t e = rtopk::launch_topk_sample(ot, os, R, k, temperature, seed, step, out_token, out_logprob,
                                                    (hipStream_t)stream);
     if (e != hipSuccess)

@@ -64,6 +64,12 @@ struct StepArgs {
     // outputs
     int32_t *out_beam, *out_token;
     float *out_score;
+    // top-k sampling drawn by row-local kernels built for k > 8 (nullable;
+    // beam 1, zero running scores): one token and log-probability per row
+    int32_t *smp_token;
+    float *smp_logprob;
+    float smp_tau;
+    uint64_t smp_seed, smp_step;
     // debug (nullable)
     float *dbg_T;
     uint32_t *dbg_hits;

@@ -66,6 +66,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "rtopk_draw.h"
 #include "rtopk_internal.h"
 
 // No implicit a*b+c contraction: a score and the bound it is compared with
@@ -1665,6 +1666,24 @@ __device__ __forceinline__ void emit_outputs(const StepArgs &a, int b, const uin
     }
 }
 
+// The outputs of batch element b from its k best keys; kernels built for
+// k > 8 also draw the top-k sample of the row when asked (one beam, zero
+// running score: the keys' scores are s_i = x_i - lse).
+template <bool BIGK>
+__device__ __forceinline__ void finish_outputs(const StepArgs &a, int b, const uint64_t *best, uint32_t kept, int lane)
+{
+    emit_outputs(a, b, best, kept, lane);
+    if constexpr (BIGK) {
+        if (a.smp_token) {
+            const bool has = (uint32_t)lane < kept;
+            const uint64_t key = has ? best[lane] : 0ull;
+            const float s = has ? from_ord((uint32_t)(key >> 32)) : -INFINITY;
+            const int32_t t = has ? (int32_t)((0xffffffffu - (uint32_t)key) % (uint32_t)a.V) : -1;
+            draw_topk_row(s, t, a.k, lane, b, a.smp_tau, a.smp_seed, a.smp_step, a.smp_token, a.smp_logprob);
+        }
+    }
+}
+
 // Wave 0 of a row-local workgroup: its rows j0..j1 of batch element b (all
 // its pieces, np = (j1 - j0 + 1) * C <= W <= 16 of them, one per lane).
 // Returns the number of keys of this workgroup's list (in `best`) and sets
@@ -1742,7 +1761,7 @@ __device__ __forceinline__ uint32_t row_select(const StepArgs &a, const SelectLd
 
     done = false;
     if (whole) { // every row of b is here
-        emit_outputs(a, b, best, kept, lane);
+        finish_outputs<BIGK>(a, b, best, kept, lane);
         return kept;
     }
     const int Lf = (int)mdiv((uint32_t)b * (uint32_t)(beam * C), a.mw);
@@ -1805,7 +1824,7 @@ __device__ __forceinline__ void row_merge(const StepArgs &a, uint64_t *keys, uin
     }
     wave_sync();
     const uint32_t nk = wave_topk<BIGK>(keys, n, k, lane, best);
-    emit_outputs(a, b, best, nk, lane);
+    finish_outputs<BIGK>(a, b, best, nk, lane);
     if (lane == 0)
         put32(ticket_of(a, b), 0u);
 }

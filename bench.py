@@ -30,7 +30,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_rtopk_step_b128.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "beam_search_top_amd", "csrc", f)
-                  for f in ("rtopk_kernels.hip", "rtopk_host.cpp", "rtopk_internal.h")]
+                  for f in ("rtopk_kernels.hip", "rtopk_host.cpp", "rtopk_internal.h", "rtopk_draw.h")]
 
 
 def kernel_sha():

@@ -223,7 +223,9 @@ int rtopk_set_row_local(int enable);
  *   out_logprob  device [R] float32: log(w_i / S), its log-probability under the
  *                top-k distribution
  * 1 <= k <= min(64, V); temperature finite and > 0. The same (seed, step) draws
- * the same tokens. Uses the library-owned workspace of `stream` (allocated on
+ * the same tokens. When the rows are selected row-locally and k > 8, the
+ * selection kernel draws right after each row's top-k (one launch); else a
+ * draw kernel follows it. Uses the library-owned workspace of `stream` (allocated on
  * the first call for a shape, like rtopk_beam_step) and a library-owned buffer
  * of zero scores per device.
  */
