@@ -82,3 +82,23 @@ def test_sample_is_reproducible_and_steps_differ():
     c = rtopk.sample_step(x, 20, 1.0, seed=9, step=5)[0].cpu().numpy()
     assert np.array_equal(a, b)
     assert (a != c).sum() > 50
+
+
+@pytest.mark.parametrize("R,V,k", [(96, 40000, 40), (64, 257, 17), (40, 20000, 64)])
+def test_fused_draw_equals_draw_kernel(R, V, k):
+    # row-local k > 8 selections draw in the selection kernel; with row-local
+    # selection off the same rows go through the separate draw kernel. Both
+    # select the same exact lists and draw with the same arithmetic.
+    rtopk.load()
+    _, x = _logits(R, V, synth.F16, seed=R * k)
+    st, p = rtopk.rtopk_plan(None, R, 1, V, k, synth.F16)
+    assert st == 0 and p.row_local
+    a = rtopk.sample_step(x, k, 0.9, seed=77, step=3)
+    assert rtopk.rtopk_set_row_local(0) == 0
+    try:
+        b = rtopk.sample_step(x, k, 0.9, seed=77, step=3)
+    finally:
+        rtopk.rtopk_set_row_local(1)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0])
+    assert torch.equal(a[1], b[1])
