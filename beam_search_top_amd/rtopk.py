@@ -149,6 +149,10 @@ def beam_step_sharded(shards, alive, finished=None, k=None, eos_id=2):
     s0 = shards[0]
     if any(t.shape != s0.shape or t.dtype != s0.dtype or not t.is_contiguous() for t in shards):
         raise ValueError("shards must be contiguous tensors of one shape and dtype")
+    if not s0.is_cuda:
+        raise ValueError("shards must be device tensors")
+    for g, t in enumerate(shards):
+        _on_device(t, s0.device, f"shard {g}")
     if k is None:
         k = s0.shape[1]
     B, beam, Vs = s0.shape
@@ -213,6 +217,13 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+def _on_device(t, dev, name):
+    """Every tensor handed to the library must live on the logits' GPU: a host
+    pointer in a kernel argument is a GPU memory fault, not an error code."""
+    if not t.is_cuda or t.device != dev:
+        raise ValueError(f"{name} must be a device tensor on {dev} (got {t.device})")
+
+
 def _prepare(logits, alive, finished, k):
     import torch
     if logits.dim() != 3:
@@ -222,19 +233,42 @@ def _prepare(logits, alive, finished, k):
     B, beam, V = logits.shape
     if not logits.is_contiguous():
         raise ValueError("logits must be contiguous")
+    dev = logits.device
+    _on_device(alive, dev, "alive")
     if alive.shape != (B, beam) or alive.dtype != torch.float32 or not alive.is_contiguous():
         raise ValueError("alive must be a contiguous float32 [B, beam] tensor")
     if finished is not None:
+        _on_device(finished, dev, "finished")
         if finished.shape != (B, beam) or finished.dtype not in (torch.uint8, torch.bool):
             raise ValueError("finished must be a [B, beam] uint8/bool tensor")
         finished = finished.contiguous()
         if finished.dtype == torch.bool:
             finished = finished.view(torch.uint8)
-    dev = logits.device
     outs = (torch.empty((B, k), dtype=torch.int32, device=dev),
             torch.empty((B, k), dtype=torch.int32, device=dev),
             torch.empty((B, k), dtype=torch.float32, device=dev))
     return B, beam, V, finished, outs
+
+
+def _check_out(out, dev, B, k):
+    """Caller-supplied outputs: (beam_ids int32, token_ids int32, scores float32), each [B, k]."""
+    import torch
+    if len(out) != 3:
+        raise ValueError("out must hold three tensors (beam_ids, token_ids, scores)")
+    for t, dt, name in zip(out, (torch.int32, torch.int32, torch.float32), ("beam_ids", "token_ids", "scores")):
+        _on_device(t, dev, f"out {name}")
+        if t.shape != (B, k) or t.dtype != dt or not t.is_contiguous():
+            raise ValueError(f"out {name} must be a contiguous {dt} [{B}, {k}] tensor")
+    return tuple(out)
+
+
+def _check_workspace(ws, dev, need):
+    import torch
+    _on_device(ws, dev, "workspace")
+    if ws.dtype != torch.uint8 or ws.dim() != 1 or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous 1-D uint8 tensor")
+    if ws.numel() < need:
+        raise ValueError(f"workspace holds {ws.numel()} bytes, {need} needed")
 
 
 def beam_step(logits, alive, finished=None, k=None, eos_id=2, workspace=None, out=None):
@@ -251,10 +285,12 @@ def beam_step(logits, alive, finished=None, k=None, eos_id=2, workspace=None, ou
         k = logits.shape[1]
     B, beam, V, finished, outs = _prepare(logits, alive, finished, k)
     if out is not None:
-        outs = out
+        outs = _check_out(out, logits.device, B, k)
     stream = torch.cuda.current_stream(logits.device).cuda_stream
     args = (_ptr(logits), dtype_code(logits), _ptr(alive), _ptr(finished), B, beam, V, k, eos_id,
             _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]))
+    if workspace is not None:
+        _check_workspace(workspace, logits.device, rtopk_workspace_bytes(B, beam, V, k, dtype_code(logits)))
     if workspace is None:
         _check(rtopk_beam_step(*args, stream))
     else:
@@ -274,6 +310,9 @@ def beam_reorder(src, dst, beam_ids):
     import torch
     if src.shape != dst.shape or src.dtype != dst.dtype or src.device != dst.device:
         raise ValueError("src and dst must have the same shape, dtype and device")
+    if not src.is_cuda:
+        raise ValueError("src and dst must be device tensors")
+    _on_device(beam_ids, src.device, "beam_ids")
     if not (src.is_contiguous() and dst.is_contiguous() and beam_ids.is_contiguous()):
         raise ValueError("src, dst and beam_ids must be contiguous")
     if beam_ids.dtype != torch.int32 or beam_ids.dim() != 2 or src.dim() < 2:

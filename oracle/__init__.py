@@ -37,24 +37,28 @@ def _load():
     global _lib
     if _lib is None:
         build()
-        L = ctypes.CDLL(_LIB)
-        vp, i32, i64, f64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
-        L.rtopk_oracle_step.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, i32]
-        L.rtopk_oracle_step.restype = i32
-        L.rtopk_oracle_lse.argtypes = [vp, i32, i64, i64, vp]
-        L.rtopk_oracle_lse.restype = None
-        L.rtopk_oracle_score_of.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32]
-        L.rtopk_oracle_score_of.restype = f64
-        L.rtopk_oracle_threshold.argtypes = [vp, i32, i64, i64, i32, i32, i64]
-        L.rtopk_oracle_threshold.restype = f64
-        L.rtopk_oracle_count_ge.argtypes = [vp, i32, i64, i64, f64]
-        L.rtopk_oracle_count_ge.restype = i64
-        L.rtopk_oracle_decode_f16.argtypes = [ctypes.c_uint16]
-        L.rtopk_oracle_decode_f16.restype = f64
-        L.rtopk_oracle_decode_bf16.argtypes = [ctypes.c_uint16]
-        L.rtopk_oracle_decode_bf16.restype = f64
-        _lib = L
+        _lib = _configure(ctypes.CDLL(_LIB))
     return _lib
+
+
+def _configure(L):
+    """Declare the argument and result types of the oracle library's entry points."""
+    vp, i32, i64, f64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+    L.rtopk_oracle_step.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, i32]
+    L.rtopk_oracle_step.restype = i32
+    L.rtopk_oracle_lse.argtypes = [vp, i32, i64, i64, vp]
+    L.rtopk_oracle_lse.restype = None
+    L.rtopk_oracle_score_of.argtypes = [vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32]
+    L.rtopk_oracle_score_of.restype = f64
+    L.rtopk_oracle_threshold.argtypes = [vp, i32, i64, i64, i32, i32, i64]
+    L.rtopk_oracle_threshold.restype = f64
+    L.rtopk_oracle_count_ge.argtypes = [vp, i32, i64, i64, f64]
+    L.rtopk_oracle_count_ge.restype = i64
+    L.rtopk_oracle_decode_f16.argtypes = [ctypes.c_uint16]
+    L.rtopk_oracle_decode_f16.restype = f64
+    L.rtopk_oracle_decode_bf16.argtypes = [ctypes.c_uint16]
+    L.rtopk_oracle_decode_bf16.restype = f64
+    return L
 
 
 def _ptr(a):

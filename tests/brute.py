@@ -35,3 +35,25 @@ def brute_topk(x64, alive, finished, k, eos_id):
             for p, (s, flat) in enumerate(ranked[:k]):
                 out_b[b, p], out_t[b, p], out_s[b][p] = flat // V, flat % V, s
     return out_b, out_t, out_s, lse
+
+
+def brute_scores(x64, alive, finished, eos_id):
+    """Every pair's score by the definition, in 50-digit decimals:
+    {(b, j, t): Decimal} for the candidates of each batch element (every token
+    of an alive beam; only (j, eos_id) of a finished beam, at its running
+    score). Pairs missing from the dict are not candidates."""
+    B, beam, V = x64.shape
+    out = {}
+    with localcontext() as ctx:
+        ctx.prec = 50
+        for b in range(B):
+            for j in range(beam):
+                a = Decimal(float(alive[b, j]))
+                if finished is not None and finished[b, j]:
+                    out[(b, j, eos_id)] = a
+                    continue
+                xs = [Decimal(float(v)) for v in x64[b, j]]
+                z = sum((xv.exp() for xv in xs), Decimal(0)).ln()
+                for t, xv in enumerate(xs):
+                    out[(b, j, t)] = a + (xv - z)
+    return out

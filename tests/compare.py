@@ -65,3 +65,38 @@ def compare(step, got_beam, got_token, got_score, ref, rtol=None, max_report=10)
         if len(problems) >= max_report:
             break
     return problems
+
+
+EXACT_REL = 1e-5  # fp64 score gap above which a position's pair is decidable exactly
+
+
+def exact_index_problems(step, got_beam, got_token, ref, ref_next, rel=EXACT_REL):
+    """Positions whose pair must match the oracle's exactly: those where the
+    oracle's fp64 score is more than rel * max(|s|, 1) away from both
+    neighbours (positions p - 1, p + 1, and for the last position the
+    (k+1)-th candidate, taken from ref_next = the oracle run with k + 1).
+    Returns (problems, accepted_swaps): accepted_swaps counts positions where
+    the pair differs from the oracle's but lies inside that window."""
+    B, k = step.B, step.k
+    got_beam = np.asarray(got_beam).reshape(B, k)
+    got_token = np.asarray(got_token).reshape(B, k)
+    s = np.asarray(ref_next.scores64).reshape(B, k + 1)
+    assert np.array_equal(np.asarray(ref_next.beam_ids)[:, :k], ref.beam_ids)
+    assert np.array_equal(np.asarray(ref_next.token_ids)[:, :k], ref.token_ids)
+    problems, swaps = [], 0
+    for b in range(B):
+        for p in range(k):
+            if ref.beam_ids[b, p] < 0:
+                continue
+            sp = s[b, p]
+            w = rel * max(abs(sp), 1.0)
+            near = (p > 0 and s[b, p - 1] - sp <= w) or (sp - s[b, p + 1] <= w)
+            same = (int(got_beam[b, p]), int(got_token[b, p])) == (int(ref.beam_ids[b, p]), int(ref.token_ids[b, p]))
+            if same:
+                continue
+            if near:
+                swaps += 1
+            else:
+                problems.append(f"b={b} p={p}: got ({got_beam[b, p]},{got_token[b, p]}), oracle "
+                                f"({ref.beam_ids[b, p]},{ref.token_ids[b, p]}) with fp64 gaps above {w:.3g}")
+    return problems, swaps

@@ -1,0 +1,43 @@
+"""Runs the oracle's pins (tests/test_oracle_pins.py) against another build of
+the oracle library, given as a path: the planted-mutation check of
+tests/test_oracle_mutants.py starts one process per mutant with this script.
+
+Exit status 0: every pin passed. 1: some pin failed (its name is printed).
+"""
+import ctypes
+import inspect
+import os
+import sys
+import traceback
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+for p in (ROOT, HERE):
+    if p not in sys.path:
+        sys.path.insert(0, p)
+
+import oracle  # noqa: E402
+
+
+def main(lib_path):
+    oracle._lib = oracle._configure(ctypes.CDLL(lib_path))
+    import test_oracle_pins as pins
+    from beam_search_top_amd import synth
+    for name, fn in sorted(inspect.getmembers(pins, inspect.isfunction), key=lambda kv: kv[1].__code__.co_firstlineno):
+        if not name.startswith("test_"):
+            continue
+        args = inspect.signature(fn).parameters
+        calls = [dict(dtype=d) for d in (synth.F32, synth.F16, synth.BF16)] if "dtype" in args else [{}]
+        for kw in calls:
+            try:
+                fn(**kw)
+            except Exception:  # an assertion of a pin (or an error it raised) catches the mutant
+                print(f"caught by {name}{kw or ''}:", traceback.format_exc(limit=1).strip().splitlines()[-1],
+                      flush=True)
+                return 1
+    print("every pin passed", flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1]))

@@ -191,3 +191,12 @@ def test_planner_workgroup_rules(lib):
     assert st == 0 and p.row_local == 1 and p.pieces_per_group == 16
     st, p = rtopk.rtopk_plan(None, 128, 4, 40000, 4, 1)  # the 4 x 40000 fp16 shape: 2 rows per workgroup
     assert st == 0 and p.row_local == 1 and p.chunks == 8 and p.pieces_per_group == 16 and p.grid == 256
+
+
+def test_binding_rejects_host_logits():
+    import torch
+    from beam_search_top_amd import rtopk
+    x = torch.zeros((2, 3, 16), dtype=torch.float16)
+    a = torch.zeros((2, 3), dtype=torch.float32)
+    with pytest.raises(ValueError):
+        rtopk.beam_step(x, a, None, k=2)

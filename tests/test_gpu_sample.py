@@ -36,6 +36,7 @@ def _logits(R, V, dtype, seed, kind="normal"):
     (128, 40000, 40, 0.8, synth.F16, "normal"), (64, 32000, 8, 1.0, synth.F32, "normal"),
     (32, 50000, 64, 1.3, synth.BF16, "gumbel"), (16, 7, 1, 1.0, synth.F32, "normal"),
     (50, 1000, 5, 0.5, synth.F16, "ties"), (300, 257, 17, 2.0, synth.BF16, "normal"),
+    (96, 40000, 12, 1.0, synth.F16, "normal"), (64, 20000, 12, 0.7, synth.BF16, "gumbel"),
 ])
 def test_sample_matches_oracle(R, V, k, tau, dtype, kind):
     # Two stages, each against the oracle: the selection's per-row top-k lists
@@ -84,7 +85,8 @@ def test_sample_is_reproducible_and_steps_differ():
     assert (a != c).sum() > 50
 
 
-@pytest.mark.parametrize("R,V,k", [(96, 40000, 40), (64, 257, 17), (40, 20000, 64)])
+@pytest.mark.parametrize("R,V,k", [(96, 40000, 40), (64, 257, 17), (40, 20000, 64), (96, 40000, 12),
+                                   (50, 30000, 9)])
 def test_fused_draw_equals_draw_kernel(R, V, k):
     # row-local k > 8 selections draw in the selection kernel; with row-local
     # selection off the same rows go through the separate draw kernel. Both
