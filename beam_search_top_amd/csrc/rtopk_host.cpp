@@ -21,6 +21,8 @@
 #include <string>
 #include <utility>
 
+static_assert(rtopk::kWsFixedBytes == RTOPK_WS_FIXED_BYTES, "the header states the fixed region's size");
+
 namespace {
 
 thread_local std::string g_err;
@@ -38,7 +40,9 @@ int fail(int status, const char *fmt, ...)
 
 std::atomic<int> g_override_nv{0};
 std::atomic<int> g_override_limit{0};
+std::atomic<int> g_override_waves{0};
 std::atomic<int> g_rowlocal{1};
+std::atomic<unsigned> g_spin_limit{rtopk::kDefaultSpinLimit};
 
 const int kVecsPerThread[] = {1, 2, 3, 4, 6, 8, 10, 12};
 // Most 16-byte vectors a lane holds without register spills and with >= 4
@@ -166,12 +170,18 @@ int make_plan(const void *logits, int B, int beam, int V, int k, int dtype, rtop
     // workgroups (measured: 512 rows x 40000 fp16, k = 40, 57 -> 39 us).
     if (g_rowlocal.load() && k >= 16 && p->waves % C == 0 && (long long)beam * C < p->waves)
         p->waves = (int)(beam * C);
-    p->grid = ceil_div(rows * C, p->waves);
     // Row-local: when a row's pieces divide the workgroup, workgroups hold
     // whole rows and select them themselves; a batch element's rows then span
     // at most maxl workgroups, which exchange one list of k keys each.
+    const int ow = g_override_waves.load();
+    if (ow > 0)
+        p->waves = ow;
+    p->grid = ceil_div(rows * C, p->waves);
     p->rowlocal = p->waves % C == 0 && g_rowlocal.load() ? 1 : 0;
     p->maxl = (int)ceil_div((long long)beam * C, p->waves) + 1;
+    // row-local lists go through the mailbox of the workspace's fixed region
+    if (p->rowlocal && (long long)B * p->maxl * k > rtopk::kMailboxSlots)
+        p->rowlocal = 0;
     if (rows * C >= (1ll << 31)) // piece indices are 31-bit in the kernel
         return fail(RTOPK_ENOTSUP, "%lld pieces are too many", rows * C);
     if ((long long)beam * C > rtopk::kMaxPieces)
@@ -194,20 +204,18 @@ int make_plan(const void *logits, int B, int beam, int V, int k, int dtype, rtop
 
     if (B > rtopk::kTicketCap)
         return fail(RTOPK_ENOTSUP, "B=%d exceeds the implementation limit %d", B, rtopk::kTicketCap);
-    // tickets first, in a region of fixed size: no shape ever stores other
-    // data there, so it stays zero between calls whatever the shapes are
-    size_t off = 0;
-    p->ws_ticket_off = off;
-    off = align256(off + sizeof(uint32_t) * (size_t)rtopk::kTicketCap);
+    // tickets, status words and the mailbox first, in a region of fixed size:
+    // no shape ever stores other data there, so it stays zero between calls
+    // whatever the shapes are; then the per-piece headers and slots
+    size_t off = align256(rtopk::kWsFixedBytes);
     p->ws_head_off = off;
-    // piece headers (two words each), or row-local list counts
-    const size_t nhead = 2 * (size_t)rows * (size_t)C > (size_t)B * p->maxl ? 2 * (size_t)rows * (size_t)C
-                                                                            : (size_t)B * p->maxl;
-    off = align256(off + sizeof(uint64_t) * nhead);
-    p->ws_slots_off = off;
-    // every piece's top-k, or row-local lists of k keys
-    const size_t nslot = (size_t)p->queue_cap > (size_t)p->maxl * k ? (size_t)p->queue_cap : (size_t)p->maxl * k;
-    off = align256(off + sizeof(uint64_t) * (size_t)B * nslot);
+    if (!p->rowlocal) {
+        off = align256(off + sizeof(uint64_t) * 2 * (size_t)rows * (size_t)C); // piece headers, two words each
+        p->ws_slots_off = off;
+        off = align256(off + sizeof(uint64_t) * (size_t)B * (size_t)p->queue_cap); // every piece's top-k
+    } else {
+        p->ws_slots_off = off;
+    }
     p->ws_bytes = off;
     return RTOPK_OK;
 }
@@ -275,8 +283,12 @@ int enqueue(const rtopk::Plan &p, const void *logits, int dtype, const float *al
     a.mb = rtopk::make_magic((uint32_t)beam);
     a.mp = rtopk::make_magic((uint32_t)beam * (uint32_t)p.chunks);
     a.mw = rtopk::make_magic((uint32_t)p.waves);
+    a.mv = rtopk::make_magic((uint32_t)V);
+    a.spin_limit = g_spin_limit.load();
     uint8_t *w = (uint8_t *)ws;
-    a.ticket = (uint32_t *)(w + p.ws_ticket_off);
+    a.ticket = (uint32_t *)(w + rtopk::kWsTicketOff);
+    a.status = (uint32_t *)(w + rtopk::kWsStatusOff);
+    a.mailbox = (uint64_t *)(w + rtopk::kWsMailboxOff);
     a.head = (uint64_t *)(w + p.ws_head_off);
     a.slots = (uint64_t *)(w + p.ws_slots_off);
     a.out_beam = ob;
@@ -539,6 +551,51 @@ int rtopk_set_row_local(int enable)
 {
     g_rowlocal.store(enable != 0 ? 1 : 0);
     return RTOPK_OK;
+}
+
+int rtopk_set_waves(int waves)
+{
+    if (waves < 0 || waves > rtopk::kMaxWaves)
+        return fail(RTOPK_EINVAL, "waves=%d outside [0, %d]", waves, rtopk::kMaxWaves);
+    g_override_waves.store(waves);
+    return RTOPK_OK;
+}
+
+int rtopk_set_spin_limit(unsigned polls)
+{
+    g_spin_limit.store(polls);
+    return RTOPK_OK;
+}
+
+int rtopk_check(void *workspace, void *stream)
+{
+    hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess)
+        return fail(RTOPK_EHIP, "hipStreamSynchronize: %s", hipGetErrorString(e));
+    void *ws = workspace;
+    if (!ws) {
+        int dev = 0;
+        if ((e = hipGetDevice(&dev)) != hipSuccess)
+            return fail(RTOPK_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+        std::lock_guard<std::mutex> lock(g_ws_mu);
+        auto it = g_ws.find({dev, stream});
+        if (it == g_ws.end() || !it->second.ptr)
+            return RTOPK_OK; // no call has run on this stream
+        ws = it->second.ptr;
+    }
+    uint32_t status = 0;
+    e = hipMemcpy(&status, (uint8_t *)ws + rtopk::kWsStatusOff, sizeof status, hipMemcpyDeviceToHost);
+    if (e != hipSuccess)
+        return fail(RTOPK_EHIP, "reading the workspace status: %s", hipGetErrorString(e));
+    if (status == 0)
+        return RTOPK_OK;
+    // a merge gave up waiting: late lists may have landed in the mailbox after
+    // the call; clear the whole fixed region so the workspace is usable again
+    if ((e = rtopk::launch_zero(ws, rtopk::kWsFixedBytes, (hipStream_t)stream)) != hipSuccess ||
+        (e = hipStreamSynchronize((hipStream_t)stream)) != hipSuccess)
+        return fail(RTOPK_EHIP, "clearing the workspace after a failed wait: %s", hipGetErrorString(e));
+    return fail(RTOPK_ETIMEOUT, "a row-local merge gave up waiting for another workgroup's list (status 0x%x); "
+                "its batch elements were written as padding; the workspace has been cleared", status);
 }
 
 int rtopk_sample_step(const void *logits, int dtype, int R, int V, int k, float temperature, uint64_t seed,

@@ -14,8 +14,22 @@ constexpr int kMaxChunkLimit = 128; // candidates a piece stages in LDS (up to t
 constexpr int kMaxSortKeys = 512;   // LDS sort keys of the per-batch selection
 constexpr int kMaxPieces = 3072;    // pieces (beam * chunks) of one batch element (LDS tables)
 constexpr int kMaxK = 64;
-constexpr int kTicketCap = 65536;
-constexpr int kMaxShards = 8;       // vocabulary shards of one sharded call   // batch elements the ticket region holds (B limit)
+constexpr int kTicketCap = 65536;   // batch elements the ticket region holds (B limit)
+constexpr int kMaxShards = 8;       // vocabulary shards of one sharded call
+// Row-local workgroups hand their lists over through a mailbox of 64-bit
+// slots that is all zero between calls; a shape whose lists do not fit it
+// takes the per-piece publication path.
+constexpr int kMailboxSlots = 1 << 17;
+constexpr uint64_t kEmptySlot = 1;  // a published slot without a key (below every real key)
+constexpr int kStatusWords = 64;    // error words of the workspace (word 0: a wait gave up)
+constexpr unsigned kDefaultSpinLimit = 1u << 22; // polls of the mailbox before a wait gives up
+
+// The part of every workspace that must be zero when a call starts and that
+// every completed call leaves zero: tickets, status words, mailbox.
+constexpr size_t kWsTicketOff = 0;
+constexpr size_t kWsStatusOff = kWsTicketOff + 4 * (size_t)kTicketCap;
+constexpr size_t kWsMailboxOff = kWsStatusOff + 4 * (size_t)kStatusWords;
+constexpr size_t kWsFixedBytes = kWsMailboxOff + 8 * (size_t)kMailboxSlots;
 
 // Division by a launch constant d >= 1 for dividends n < 2^31:
 // floor(n / d) = (n * mul) >> shr with shr = 31 + ceil(log2 d) and
@@ -50,15 +64,18 @@ struct StepArgs {
     int waves;                     // pieces (waves) per workgroup, <= kMaxWaves
     int rowlocal;                  // workgroups hold whole rows (chunks divides waves)
     int maxl;                      // row-local: workgroup lists per batch element, at most
-    Magic mc, mb, mp, mw;          // division by chunks, beam, beam*chunks, waves
+    unsigned spin_limit;           // row-local: polls of the mailbox before the merge gives up
+    Magic mc, mb, mp, mw, mv;      // division by chunks, beam, beam*chunks, waves, V
     // Vocabulary shards: a row's pieces g*cps .. g*cps + cps - 1 lie in shard g,
     // whose [B][beam][vshard] tensor starts at shard[g] (one shard: shard[0] is
     // logits_aligned, vshard = V, cps = chunks). Token t of shard g is g*vshard + t.
     int vshard, cps;
     Magic ms;                      // division by cps
     const uint8_t *shard[kMaxShards];
-    // workspace; only the ticket region must be zero when a call starts
+    // workspace; only the fixed region (tickets, status, mailbox) must be zero when a call starts
     uint32_t *ticket;              // [kTicketCap] arrivals, first B used
+    uint32_t *status;              // [kStatusWords] sticky error words
+    uint64_t *mailbox;             // row-local lists [B][maxl][k] (kEmptySlot pads a short list)
     uint64_t *head;                // [B*beam*chunks][2]: (max2 | sum << 32), (threshold | count << 32)
     uint64_t *slots;               // [B*beam*chunks][k] each piece's top-k sort keys by logit
     // outputs
@@ -85,7 +102,7 @@ struct Plan {
     int nshards, vshard, cps; // vocabulary shards, logits per shard row, pieces per shard row
     long long grid;
     size_t lds_bytes;
-    size_t ws_ticket_off, ws_head_off, ws_slots_off, ws_bytes;
+    size_t ws_head_off, ws_slots_off, ws_bytes;
 };
 
 // Enqueue the fused select + sort kernel for logits of type DT (0 float32,
@@ -112,11 +129,11 @@ bool supported_vecs_per_thread(int nv);
 size_t group_lds_bytes(int waves, size_t sort_bytes, bool rowlocal, int k, int maxl);
 
 // Row-local workgroups: LDS keys of the workgroup's own selection (every
-// candidate of its pieces plus one per finished row) and of the final merge
-// (every list of a batch element).
+// candidate of its pieces plus one per finished row) followed, in the
+// workgroup that merges, by the other workgroups' lists.
 __host__ __device__ constexpr int rowlocal_keys(int waves, int k, int maxl)
 {
-    return waves * (k + 1) > maxl * k ? waves * (k + 1) : maxl * k;
+    return waves * (k + 1) + maxl * k;
 }
 
 } // namespace rtopk

@@ -174,23 +174,16 @@ __device__ __forceinline__ void drain_stores()
 // crosses an integer boundary before the truncation.
 __device__ __forceinline__ int small_div(int q, float inv_d) { return (int)(((float)q + 0.5f) * inv_d); }
 
-// ---------------------------------------------------------------- XCD placement
+// ---------------------------------------------------------------- XCD grouping
 // Workgroups are dispatched to the 8 XCDs round robin (workgroup w on XCD
-// w mod 8), and each XCD has its own L2. Workgroup w takes the pieces of
-// logical workgroup L(w), which groups consecutive logical workgroups -- hence
-// the pieces of a batch element -- on one XCD. Nothing relies on this for
-// correctness: the XCD a workgroup actually runs on is read from the hardware
-// and reported with its arrival (see rtopk_step).
+// w mod 8), and each XCD has its own L2 and address translation caches.
+// Workgroup w takes the pieces of logical workgroup L(w), which gives every
+// XCD one contiguous eighth of the tensor (the last G mod 8 workgroups keep
+// their index). A bijection on [0, G); nothing relies on it for correctness.
 constexpr int kXcds = 8;
-__device__ __forceinline__ uint32_t xcc_id()
-{
-    uint32_t x;
-    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
-    return x & 0xfu;
-}
 __device__ __forceinline__ int logical_group(int w, int G)
 {
-    const uint32_t uw = (uint32_t)w, G8 = (uint32_t)G & ~(uint32_t)(kXcds - 1); // the last G mod 8 keep their index
+    const uint32_t uw = (uint32_t)w, G8 = (uint32_t)G & ~(uint32_t)(kXcds - 1);
     return uw < G8 ? (int)((uw % kXcds) * (G8 / kXcds) + uw / kXcds) : w;
 }
 
@@ -199,12 +192,6 @@ __device__ __forceinline__ uint32_t mdiv(uint32_t n, Magic m)
 {
     return (uint32_t)(((uint64_t)n * m.mul) >> m.shr);
 }
-__device__ __forceinline__ int xcd_of_logical(int L, int G)
-{
-    const int G8 = G - G % kXcds;
-    return L < G8 ? L / (G8 / kXcds) : L % kXcds;
-}
-
 // ---------------------------------------------------------------- wave primitives
 __device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
 
@@ -374,7 +361,24 @@ template <> struct Traits<0> { // float32
     {
         return fmaxf(fmaxf(elem(d, 0), elem(d, 1)), fmaxf(elem(d, 2), elem(d, 3))) >= T;
     }
+    // element 0, and the vector moved down by one element (rolled loops)
+    __device__ static float first(const uint4 &d) { return __uint_as_float(d.x); }
+    __device__ static void shift(uint4 &d)
+    {
+        d.x = d.y;
+        d.y = d.z;
+        d.z = d.w;
+    }
 };
+
+// Moves a vector of 16-bit elements down by one element.
+__device__ __forceinline__ void shift16(uint4 &d)
+{
+    d.x = __builtin_amdgcn_alignbit(d.y, d.x, 16);
+    d.y = __builtin_amdgcn_alignbit(d.z, d.y, 16);
+    d.z = __builtin_amdgcn_alignbit(d.w, d.z, 16);
+    d.w >>= 16;
+}
 
 template <> struct Traits<1> { // float16, max kept on packed pairs
     static constexpr int epv = 8;
@@ -437,6 +441,8 @@ template <> struct Traits<1> { // float16, max kept on packed pairs
         const _Float16 th = (_Float16)T;
         return __builtin_fmaxf16(t.x, t.y) >= th; // one compare: its lane mask is the ballot
     }
+    __device__ static float first(const uint4 &d) { return (float)__builtin_bit_cast(_Float16, (uint16_t)d.x); }
+    __device__ static void shift(uint4 &d) { shift16(d); }
 };
 
 template <> struct Traits<2> { // bfloat16: widened to fp32 by a shift or a mask
@@ -496,7 +502,24 @@ template <> struct Traits<2> { // bfloat16: widened to fp32 by a shift or a mask
             m = fmaxf(m, elem(d, i));
         return m >= T;
     }
+    __device__ static float first(const uint4 &d) { return __uint_as_float(d.x << 16); }
+    __device__ static void shift(uint4 &d) { shift16(d); }
 };
+
+// d[r] for a wave-uniform r, by selects (no indexing of the register array).
+template <int NV> __device__ __forceinline__ uint4 pick(const uint4 (&d)[NV], int r)
+{
+    uint4 v = d[0];
+#pragma unroll
+    for (int i = 1; i < NV; ++i) {
+        const bool s = r == i;
+        v.x = s ? d[i].x : v.x;
+        v.y = s ? d[i].y : v.y;
+        v.z = s ? d[i].z : v.z;
+        v.w = s ? d[i].w : v.w;
+    }
+    return v;
+}
 
 // ------------------------------------------------------------ passes 1 and 2
 // Read in place of the finished mask when there is none (0), or in place of a
@@ -544,10 +567,22 @@ struct SelectLds {
 };
 static_assert(sizeof(SelectLds) % 16 == 0, "per-wave LDS regions stay 16-byte aligned");
 
-// u: the piece (wave-uniform), row0: the first row of the workgroup.
-template <int DT, int NV, int MODE, bool RL>
-__device__ __forceinline__ void select_piece(const StepArgs &a, SelectLds &sm, uint32_t *gshare_rows, uint32_t u,
-                                             bool valid, uint32_t row0, int lane)
+// One wave's piece between its loads and its computation: the 16-byte vectors
+// in flight and the wave-uniform facts about the piece.
+template <int NV> struct Piece {
+    uint4 d[NV];
+    uint32_t fin;     // the row's finished flag (1 past the last piece)
+    float alv;        // the row's running score (row-local kernels)
+    uint32_t row, flat0;
+    int lead, pbeg, pend;
+    uint32_t *gshare; // the row's shared group maxima
+};
+
+// Issues the loads of piece u (wave-uniform); row0: the first row of the
+// workgroup.
+template <int DT, int NV, bool RL>
+__device__ __forceinline__ void piece_load(const StepArgs &a, Piece<NV> &P, uint32_t *gshare_rows, uint32_t u,
+                                           bool valid, uint32_t row0, int lane)
 {
     using Tr = Traits<DT>;
     constexpr int EPV = Tr::epv;
@@ -559,8 +594,9 @@ __device__ __forceinline__ void select_piece(const StepArgs &a, SelectLds &sm, u
     const int g = (int)mdiv((uint32_t)cr, a.ms);          // its vocabulary shard
     const int c = cr - g * a.cps;                         // piece of the shard's row
     const int j = (int)(row - mdiv(row, a.mb) * (uint32_t)a.beam);
+    P.row = row;
     // this row's shared group maxima (rows are counted from the workgroup's first)
-    uint32_t *gshare = gshare_rows + (row - row0) * kMaxK;
+    P.gshare = gshare_rows + (row - row0) * kMaxK;
     // Vectors are counted in the 16-byte-aligned frame of the tensor; a row
     // starts `lead` elements into its first vector v0 and spans `span` vectors.
     // Everything per lane is 32-bit and relative to the row.
@@ -571,20 +607,23 @@ __device__ __forceinline__ void select_piece(const StepArgs &a, SelectLds &sm, u
     const int span = (lead + VS + EPV - 1) / EPV;
     const int pbeg = c * a.vecs_per_chunk; // piece start, vectors from v0
     const int pend = pbeg + a.vecs_per_chunk < span ? pbeg + a.vecs_per_chunk : span;
+    P.lead = lead;
+    P.pbeg = pbeg;
+    P.pend = pend;
     // flat index j*V + vocabulary index of slot 0 of vector 0
-    const uint32_t flat0 = (uint32_t)j * (uint32_t)a.V + (uint32_t)g * (uint32_t)VS - (uint32_t)lead;
+    P.flat0 = (uint32_t)j * (uint32_t)a.V + (uint32_t)g * (uint32_t)VS - (uint32_t)lead;
 
     // The finished flag is loaded first but tested only once the piece's
     // loads are in flight: its latency under a full memory system overlaps
     // the stream instead of delaying it. The compiler fence keeps the loads
     // on their side of the test (a finished row reads its piece for nothing).
     const uint8_t *finp = !valid ? &kFlagConst[1] : a.finished != nullptr ? &a.finished[row] : &kFlagConst[0];
-    uint32_t fin = *finp;
+    P.fin = *finp;
     // row-local workgroups select their rows themselves: the row's score is
     // loaded here too, its latency hidden under the stream like the flag's
-    float alv = 0.f;
+    P.alv = 0.f;
     if constexpr (RL)
-        alv = a.alive[row];
+        P.alv = a.alive[row];
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     // Buffer loads through a descriptor that spans exactly the piece: a slot
     // past its end reads 0 without touching memory, so the loads need no
@@ -597,12 +636,26 @@ __device__ __forceinline__ void select_piece(const StepArgs &a, SelectLds &sm, u
     const uint32_t nbytes = valid && pend > pbeg ? (uint32_t)(pend - pbeg) * 16u : 0u;
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t *>(a.shard[g]) + (v0 + (uint64_t)pbeg) * 16u, 0, nbytes, 0x00020000);
-    uint4 d[NV];
 #pragma unroll
     for (int r = 0; r < NV; ++r) {
         const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rsrc, lane * 16, r * kLanes * 16, kBufNT);
-        d[r] = make_uint4(w.x, w.y, w.z, w.w);
+        P.d[r] = make_uint4(w.x, w.y, w.z, w.w);
     }
+}
+
+// Passes 1 and 2 of piece u over the vectors piece_load issued, and its top-k.
+template <int DT, int NV, int MODE, bool RL>
+__device__ __forceinline__ void piece_compute(const StepArgs &a, SelectLds &sm, Piece<NV> &P, uint32_t u, int lane)
+{
+    using Tr = Traits<DT>;
+    constexpr int EPV = Tr::epv;
+    uint4 (&d)[NV] = P.d;
+    const uint32_t row = P.row;
+    const int lead = P.lead, pbeg = P.pbeg, pend = P.pend, VS = a.vshard;
+    const uint32_t flat0 = P.flat0;
+    uint32_t *gshare = P.gshare;
+    const float alv = P.alv;
+    uint32_t fin = P.fin;
     asm volatile("" : "+v"(fin)); // the test waits for the flag here, past the loads
     if (fin != 0) {
         if (RL && lane == 0) { // an empty piece for the workgroup's own selection
@@ -740,39 +793,42 @@ __device__ __forceinline__ void select_piece(const StepArgs &a, SelectLds &sm, u
     // ---- pass 2: stage the sort key of every valid logit >= T. The wave
     // tests each of its vectors with one packed maximum; only a vector in
     // which some lane holds a hit (a wave-uniform branch, usually taken once
-    // or twice per piece) is examined element by element. Hits are ranked by
-    // ballot + mbcnt, so the count is wave-uniform and no atomics are needed.
-    // With T finite, slots outside the row or piece (set to -inf in pass 1)
-    // cannot reach it: a vector's elements are tested by independent
-    // compares straight into lane masks, and only the elements that hit
-    // somewhere are staged. T = -inf (a row without k finite logits) takes
-    // the element-by-element test with the explicit bounds.
+    // or twice per piece) is examined element by element: one compare per
+    // element straight into a lane mask, and only the elements that hit
+    // somewhere are staged. Hits are ranked by ballot + mbcnt, so the count is
+    // wave-uniform and no atomics are needed. With T finite, slots outside
+    // the row or piece (set to -inf in pass 1) cannot reach it. T = -inf (a
+    // piece without k finite logits) is rare and takes a compact rolled loop
+    // that checks each element's position.
     const uint32_t cap = (uint32_t)a.chunk_limit;
+    auto in_piece = [&](int q, int e) { // vector q (from v0), element e of the aligned frame
+        const int t = e - lead;
+        return q < pend && (MODE != kGeneral || (t >= 0 && t < VS));
+    };
     uint32_t wn = 0;
     if (ballot(tmax >= T) != 0) {
         int qb0 = pbeg + lane; // opaque: keeps per-element index math inside this block
         asm volatile("" : "+v"(qb0));
-        const bool tfin = T > -INFINITY;
-        // per vector, the lanes holding a hit: in row-local kernels all the
-        // (independent) compares first; the others, whose tail already fills
-        // the registers, test each vector as they go
-        uint64_t vm[NV];
-        if constexpr (RL > 0) {
+        if (T > -INFINITY) {
+            // per vector, the lanes holding a hit: in row-local kernels all the
+            // (independent) compares first; the others, whose tail already fills
+            // the registers, test each vector as they go
+            uint64_t vm[NV];
+            if constexpr (RL) {
+#pragma unroll
+                for (int r = 0; r < NV; ++r) {
+                    opaque(d[r]);
+                    vm[r] = ballot(Tr::any_ge(d[r], T));
+                }
+            }
 #pragma unroll
             for (int r = 0; r < NV; ++r) {
-                opaque(d[r]);
-                vm[r] = ballot(Tr::any_ge(d[r], T));
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < NV; ++r) {
-            if constexpr (!RL) {
-                opaque(d[r]);
-                vm[r] = ballot(Tr::any_ge(d[r], T));
-            }
-            if (vm[r] != 0) {
-                const int q = qb0 + r * kLanes;
-                if (tfin) {
+                if constexpr (!RL) {
+                    opaque(d[r]);
+                    vm[r] = ballot(Tr::any_ge(d[r], T));
+                }
+                if (vm[r] != 0) {
+                    const int q = qb0 + r * kLanes;
                     uint64_t mk[EPV];
 #pragma unroll
                     for (int i = 0; i < EPV; ++i)
@@ -786,20 +842,24 @@ __device__ __forceinline__ void select_piece(const StepArgs &a, SelectLds &sm, u
                             wn += (uint32_t)__builtin_popcountll(mk[i]);
                         }
                     }
-                } else {
-                    const bool inq = q < pend;
-#pragma unroll
-                    for (int i = 0; i < EPV; ++i) {
-                        const float x = Tr::elem(d[r], i);
-                        const int t = q * EPV + i - lead;
-                        const bool h = x >= T && inq && (MODE != kGeneral || (t >= 0 && t < VS));
-                        const uint64_t m = ballot(h);
-                        if (m != 0) {
-                            const uint32_t pos = wn + lane_prefix(m);
-                            if (h && pos < cap)
-                                sm.stage[pos] = score_key(x, flat0 + (uint32_t)(q * EPV + i));
-                            wn += (uint32_t)__builtin_popcountll(m);
-                        }
+                }
+            }
+        } else {
+#pragma unroll 1
+            for (int r = 0; r < NV; ++r) {
+                uint4 w = pick(d, r);
+                const int q = qb0 + r * kLanes;
+#pragma unroll 1
+                for (int i = 0, e = q * EPV; i < EPV; ++i, ++e) {
+                    const float x = Tr::first(w);
+                    Tr::shift(w);
+                    const bool h = x >= T && in_piece(q, e);
+                    const uint64_t m = ballot(h);
+                    if (m != 0) {
+                        const uint32_t pos = wn + lane_prefix(m);
+                        if (h && pos < cap)
+                            sm.stage[pos] = score_key(x, flat0 + (uint32_t)e);
+                        wn += (uint32_t)__builtin_popcountll(m);
                     }
                 }
             }
@@ -812,37 +872,35 @@ __device__ __forceinline__ void select_piece(const StepArgs &a, SelectLds &sm, u
     // values down from the top (one round when the top value repeats k
     // times); then stage every logit > v and the first k - #(> v) logits == v
     // in flat order (vectors, then lanes, then elements). That is exactly the
-    // piece's top-k by (logit desc, flat asc).
+    // piece's top-k by (logit desc, flat asc). A rare path: rolled loops.
     uint32_t nst = wn; // staged keys
     if (wn > cap) {
-        int qb0 = pbeg + lane; // opaque: keeps per-element index math inside this block
-        asm volatile("" : "+v"(qb0));
-        auto valid = [&](int r, int i) {
-            const int q = qb0 + r * kLanes;
-            const int t = q * EPV + i - lead;
-            return q < pend && (MODE != kGeneral || (t >= 0 && t < VS));
-        };
         float prev = INFINITY, v = -INFINITY;
         uint32_t above = 0;
         for (int round = 0; round < a.k; ++round) { // wn > cap >= k valid logits are >= T
             float mx = -INFINITY;
-#pragma unroll
+#pragma unroll 1
             for (int r = 0; r < NV; ++r) {
-                opaque(d[r]);
-#pragma unroll
-                for (int i = 0; i < EPV; ++i) {
-                    const float x = Tr::elem(d[r], i);
-                    mx = valid(r, i) && x < prev ? fmaxf(mx, x) : mx;
+                uint4 w = pick(d, r);
+                const int q = pbeg + lane + r * kLanes;
+#pragma unroll 1
+                for (int i = 0, e = q * EPV; i < EPV; ++i, ++e) {
+                    const float x = Tr::first(w);
+                    Tr::shift(w);
+                    mx = in_piece(q, e) && x < prev ? fmaxf(mx, x) : mx;
                 }
             }
             v = wave_max_f(mx);
             uint32_t c = 0;
-#pragma unroll
+#pragma unroll 1
             for (int r = 0; r < NV; ++r) {
-                opaque(d[r]);
-#pragma unroll
-                for (int i = 0; i < EPV; ++i)
-                    c += valid(r, i) && Tr::elem(d[r], i) == v;
+                uint4 w = pick(d, r);
+                const int q = pbeg + lane + r * kLanes;
+#pragma unroll 1
+                for (int i = 0, e = q * EPV; i < EPV; ++i, ++e) {
+                    c += in_piece(q, e) && Tr::first(w) == v;
+                    Tr::shift(w);
+                }
             }
             c = wave_sum_u32(c);
             if (above + c >= (uint32_t)a.k)
@@ -851,41 +909,45 @@ __device__ __forceinline__ void select_piece(const StepArgs &a, SelectLds &sm, u
             prev = v;
         }
         nst = 0;
-#pragma unroll
-        for (int r = 0; r < NV; ++r) { // the logits > v
-            opaque(d[r]);
-            const int q = qb0 + r * kLanes;
-#pragma unroll
-            for (int i = 0; i < EPV; ++i) {
-                const float x = Tr::elem(d[r], i);
-                const bool h = valid(r, i) && x > v;
+#pragma unroll 1
+        for (int r = 0; r < NV; ++r) { // the logits > v (fewer than k)
+            uint4 w = pick(d, r);
+            const int q = pbeg + lane + r * kLanes;
+#pragma unroll 1
+            for (int i = 0, e = q * EPV; i < EPV; ++i, ++e) {
+                const float x = Tr::first(w);
+                Tr::shift(w);
+                const bool h = in_piece(q, e) && x > v;
                 const uint64_t m = ballot(h);
                 if (m != 0) {
                     if (h)
-                        sm.stage[nst + lane_prefix(m)] = score_key(x, flat0 + (uint32_t)(q * EPV + i));
+                        sm.stage[nst + lane_prefix(m)] = score_key(x, flat0 + (uint32_t)e);
                     nst += (uint32_t)__builtin_popcountll(m);
                 }
             }
         }
         uint32_t need = (uint32_t)a.k - above;
-#pragma unroll
-        for (int r = 0; r < NV; ++r) { // the first `need` logits == v
-            if (need == 0) // uniform; no break, so the loop unrolls and d[] stays in registers
-                continue;
-            opaque(d[r]);
-            const int q = qb0 + r * kLanes;
+#pragma unroll 1
+        for (int r = 0; r < NV && need != 0; ++r) { // the first `need` logits == v
+            const uint4 w0 = pick(d, r);
+            const int q = pbeg + lane + r * kLanes;
+            uint4 w = w0;
             uint32_t bits = 0;
-#pragma unroll
-            for (int i = 0; i < EPV; ++i)
-                bits |= (uint32_t)(valid(r, i) && Tr::elem(d[r], i) == v) << i;
+#pragma unroll 1
+            for (int i = 0, e = q * EPV; i < EPV; ++i, ++e) {
+                bits |= (uint32_t)(in_piece(q, e) && Tr::first(w) == v) << i;
+                Tr::shift(w);
+            }
             const uint32_t cnt = (uint32_t)__builtin_popcount(bits);
             const uint32_t before = wave_excl_scan_u32(cnt, lane);
             const uint32_t total = first_u32(__builtin_amdgcn_readlane(before + cnt, 63));
-#pragma unroll
-            for (int i = 0; i < EPV; ++i) {
+            w = w0;
+#pragma unroll 1
+            for (int i = 0, e = q * EPV; i < EPV; ++i, ++e) {
                 const uint32_t rank = before + (uint32_t)__builtin_popcount(bits & ((1u << i) - 1u));
                 if (((bits >> i) & 1u) && rank < need)
-                    sm.stage[nst + rank] = score_key(Tr::elem(d[r], i), flat0 + (uint32_t)(q * EPV + i));
+                    sm.stage[nst + rank] = score_key(Tr::first(w), flat0 + (uint32_t)e);
+                Tr::shift(w);
             }
             const uint32_t took = total < need ? total : need;
             nst += took;
@@ -991,8 +1053,7 @@ struct SortLds {
 
 // Counters and reduction scratch of a workgroup, in front of its LDS.
 struct GroupLds {
-    uint32_t todo[2];  // batch elements whose ticket this workgroup completed
-    uint32_t local[2]; // ... of which every piece was published on this workgroup's XCD
+    uint32_t todo[2]; // batch elements whose ticket this workgroup completed
     uint32_t ns, ndbg;
     float fred[kMaxWaves];
     uint64_t kred[kMaxWaves];
@@ -1149,7 +1210,7 @@ __device__ __forceinline__ void sort_batch(const StepArgs &a, const SortLds &sm,
     float bound = -INFINITY;
     for (int jj = tid; jj < beam; jj += nth) {
         const float alv = sm.alive[jj];
-        float lse = __uint_as_float(0x7fc00000u), thr = INFINITY; // NaN marks a finished beam
+        float lse = 0.f, thr = INFINITY; // a finished beam's thr keeps its slots out
         if (!sm.fin[jj]) {
             lse = (sm.pm[jj * C] + fast_log2(sm.ps[jj * C])) * kLn2;
             thr = sm.pt[jj * C];
@@ -1159,8 +1220,8 @@ __device__ __forceinline__ void sort_batch(const StepArgs &a, const SortLds &sm,
         }
         sm.lse[jj] = lse;
         sm.thr[jj] = thr;
-        if (a.dbg_lse)
-            a.dbg_lse[b * beam + jj] = lse;
+        if (a.dbg_lse) // NaN bits mark a finished beam
+            reinterpret_cast<uint32_t *>(a.dbg_lse)[b * beam + jj] = sm.fin[jj] ? 0x7fc00000u : __float_as_uint(lse);
     }
     bound = block_max_f(bound, g, lane, wave, W); // its barriers also publish the tables
 
@@ -1333,7 +1394,7 @@ template <int LEVEL> __device__ __forceinline__ void merge_level(float &m, float
 // beam's partials are merged by DPP butterflies over its lanes (C a power of
 // two <= 16) or by a fixed tree in LDS; survivors are ranked by ballot with
 // the count in a scalar register. No barriers, no LDS atomics.
-__device__ __forceinline__ void sort_batch_wave(const StepArgs &a, const SortLds &sm, int b, int lane, bool local)
+__device__ __forceinline__ void sort_batch_wave(const StepArgs &a, const SortLds &sm, int b, int lane)
 {
     const int beam = a.beam, C = a.chunks, L = a.k;
     const int P = beam * C, NS = P * L;
@@ -1345,36 +1406,17 @@ __device__ __forceinline__ void sort_batch_wave(const StepArgs &a, const SortLds
     const float invC = 1.f / (float)C, invL = 1.f / (float)L;
 
     // ---- one round trip: 4 slots per lane, this lane's piece header, its beam's
-    // flag and score. When every piece was published on this XCD, its L2 holds
-    // the data: loads that skip only the CU's L1 (sc0); otherwise
-    // device-coherent loads that skip the L2 too (sc1).
+    // flag and score (device-coherent loads)
     uint64_t spec[4];
     const bool own = lane < P;
     const int jp = own ? small_div(lane, invC) : 0; // this lane's beam
-    uint64_t h0 = 0, h1 = 0;
-    if (local) {
-        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint64_t *>(slots), 0, 8 * NS, 0x00020000);
-        const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint64_t *>(head), 0, 16 * P, 0x00020000);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) { // loads past num_records read 0
-            const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, 8 * (lane + r * kLanes), 0, 1);
-            spec[r] = ((uint64_t)v[1] << 32) | v[0];
-        }
-        const auto v0 = __builtin_amdgcn_raw_buffer_load_b64(rh, 16 * lane, 0, 1);
-        const auto v1 = __builtin_amdgcn_raw_buffer_load_b64(rh, 16 * lane + 8, 0, 1);
-        h0 = ((uint64_t)v0[1] << 32) | v0[0];
-        h1 = ((uint64_t)v1[1] << 32) | v1[0];
-    } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int gi = lane + r * kLanes;
-            spec[r] = gi < NS ? get64(&slots[gi]) : 0ull;
-        }
-        h0 = own ? get64(&head[2 * lane]) : 0ull;
-        h1 = own ? get64(&head[2 * lane + 1]) : 0ull;
+    for (int r = 0; r < 4; ++r) {
+        const int gi = lane + r * kLanes;
+        spec[r] = gi < NS ? get64(&slots[gi]) : 0ull;
     }
+    const uint64_t h0 = own ? get64(&head[2 * lane]) : 0ull;
+    const uint64_t h1 = own ? get64(&head[2 * lane + 1]) : 0ull;
     const float alv = own ? a.alive[b * beam + jp] : 0.f;
     const bool fin = own && has_fin && finb[jp] != 0;
     float m = own ? __uint_as_float((uint32_t)h0) : -INFINITY;
@@ -1417,7 +1459,7 @@ __device__ __forceinline__ void sort_batch_wave(const StepArgs &a, const SortLds
         }
         wave_sync(); // every lane has read before the tables below are rewritten
     }
-    const float lse = fin ? __uint_as_float(0x7fc00000u) : (m + fast_log2(sum)) * kLn2; // NaN: finished
+    const float lse = fin ? 0.f : (m + fast_log2(sum)) * kLn2; // unused for a finished beam
     const float thr = fin ? INFINITY : t;
     // at least k logits of a beam are >= thr, so at least k candidates score >= alive + (thr - lse)
     const float bound = wave_max_f(own && !fin ? alv + (thr - lse) : -INFINITY);
@@ -1431,8 +1473,8 @@ __device__ __forceinline__ void sort_batch_wave(const StepArgs &a, const SortLds
         sm.pn[lane] = (uint8_t)pn;
         if (lane == jp * C) {
             sm.fin[jp] = (uint8_t)fin;
-            if (a.dbg_lse)
-                a.dbg_lse[b * beam + jp] = lse;
+            if (a.dbg_lse) // NaN bits mark a finished beam
+                reinterpret_cast<uint32_t *>(a.dbg_lse)[b * beam + jp] = fin ? 0x7fc00000u : __float_as_uint(lse);
         }
     }
     wave_sync();
@@ -1654,7 +1696,7 @@ __device__ __forceinline__ void emit_outputs(const StepArgs &a, int b, const uin
         if ((uint32_t)p < kept) {
             const uint64_t key = best[p];
             const uint32_t flat = 0xffffffffu - (uint32_t)key;
-            const uint32_t jj = flat / (uint32_t)a.V;
+            const uint32_t jj = mdiv(flat, a.mv);
             a.out_beam[o] = (int32_t)jj;
             a.out_token[o] = (int32_t)(flat - jj * (uint32_t)a.V);
             a.out_score[o] = from_ord((uint32_t)(key >> 32));
@@ -1678,30 +1720,23 @@ __device__ __forceinline__ void finish_outputs(const StepArgs &a, int b, const u
             const bool has = (uint32_t)lane < kept;
             const uint64_t key = has ? best[lane] : 0ull;
             const float s = has ? from_ord((uint32_t)(key >> 32)) : -INFINITY;
-            const int32_t t = has ? (int32_t)((0xffffffffu - (uint32_t)key) % (uint32_t)a.V) : -1;
+            const uint32_t flat = 0xffffffffu - (uint32_t)key;
+            const int32_t t = has ? (int32_t)(flat - mdiv(flat, a.mv) * (uint32_t)a.V) : -1;
             draw_topk_row(s, t, a.k, lane, b, a.smp_tau, a.smp_seed, a.smp_step, a.smp_token, a.smp_logprob);
         }
     }
 }
 
 // Wave 0 of a row-local workgroup: its rows j0..j1 of batch element b (all
-// its pieces, np = (j1 - j0 + 1) * C <= W <= 16 of them, one per lane).
-// Returns the number of keys of this workgroup's list (in `best`) and sets
-// `done` when this workgroup arrived last among those holding rows of b and
-// every other list is published; the caller then runs row_merge.
-template <bool BIGK>
-__device__ __forceinline__ uint32_t row_select(const StepArgs &a, const SelectLds *wl, uint64_t *keys, uint64_t *best,
-                                           uint32_t ufirst, int LG, int b, int j0, int j1, int lane,
-                                           bool &done)
+// their pieces, np = (j1 - j0 + 1) * C <= W <= 16 of them, one per lane).
+// Merges each row's partials, and puts into keys[0..n) the sort keys of its
+// candidates that can be among b's top-k: at least k of them score >= the
+// bound S = max over its alive rows of alive + (threshold - lse), so no
+// candidate below S can. Returns n.
+__device__ __forceinline__ uint32_t row_candidates(const StepArgs &a, const SelectLds *wl, uint64_t *keys,
+                                                   uint32_t ufirst, int b, int j0, int j1, int lane)
 {
     const int C = a.chunks, beam = a.beam, k = a.k;
-    // A batch element whose rows span several workgroups: report this
-    // workgroup's arrival first, so that the atomic's round trip overlaps the
-    // selection below. Low 16 bits count arrivals, high 16 bits publications.
-    const bool whole = j0 == 0 && j1 == beam - 1;
-    uint32_t arrived = 0;
-    if (!whole && lane == 0)
-        arrived = __hip_atomic_fetch_add(ticket_of(a, b), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int nrows = j1 - j0 + 1, np = nrows * C;
     const long long p0 = ((long long)b * beam + j0) * C; // first piece
     const bool own = lane < np;
@@ -1719,13 +1754,11 @@ __device__ __forceinline__ uint32_t row_select(const StepArgs &a, const SelectLd
         merge_level<2>(m, sum, t);
     if (C >= 16)
         merge_level<3>(m, sum, t);
-    const float lse = fin ? __uint_as_float(0x7fc00000u) : (m + fast_log2(sum)) * kLn2; // NaN: finished
+    const float lse = fin ? 0.f : (m + fast_log2(sum)) * kLn2; // unused for a finished row
     const float thr = fin ? INFINITY : t;
-    // at least k logits of an alive row are >= thr: at least k candidates of
-    // this workgroup score >= its bound
     const float bound = wave_max_f(own && !fin ? alv + (thr - lse) : -INFINITY);
-    if (a.dbg_lse && own && lane == jl * C)
-        a.dbg_lse[(long long)b * beam + j] = lse;
+    if (a.dbg_lse && own && lane == jl * C) // NaN bits mark a finished row
+        reinterpret_cast<uint32_t *>(a.dbg_lse)[(long long)b * beam + j] = fin ? 0x7fc00000u : __float_as_uint(lse);
 
     // survivors -> keys, by ballot (ns is wave-uniform)
     uint32_t ns = 0;
@@ -1756,77 +1789,110 @@ __device__ __forceinline__ uint32_t row_select(const StepArgs &a, const SelectLd
         const bool ok = first && fin && alv >= bound;
         offer(ok, ok ? score_key(alv, (uint32_t)j * (uint32_t)a.V + (uint32_t)a.eos_id) : 0ull);
     }
-    wave_sync();
-    const uint32_t kept = wave_topk<BIGK>(keys, ns, k, lane, best);
-
-    done = false;
-    if (whole) { // every row of b is here
-        finish_outputs<BIGK>(a, b, best, kept, lane);
-        return kept;
-    }
-    const int Lf = (int)mdiv((uint32_t)b * (uint32_t)(beam * C), a.mw);
-    const int Ll = (int)mdiv(((uint32_t)b + 1) * (uint32_t)(beam * C) - 1, a.mw);
-    const uint32_t nl = (uint32_t)(Ll - Lf + 1); // workgroups holding rows of b
-    arrived = first_u32(arrived);
-    if ((arrived & 0xffffu) + 1u < nl) {
-        // not the last to arrive: publish this workgroup's list, then count
-        // the publication once its stores are performed
-        uint64_t *list = a.slots + ((long long)b * a.maxl + (LG - Lf)) * k;
-        for (int p = lane; p < (int)kept; p += kLanes)
-            put64(&list[p], best[p]);
-        if (lane == 0)
-            put64(&a.head[(long long)b * a.maxl + (LG - Lf)], kept);
-        drain_stores();
-        if (lane == 0)
-            __hip_atomic_fetch_add(ticket_of(a, b), 1u << 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        return kept;
-    }
-    // The last to arrive merges. Every other workgroup of b arrived before
-    // it, so each is running its selection and will publish: wait until the
-    // nl - 1 publications are counted (usually already true at the arrival,
-    // else a few polls). The cap only bounds the loop; it is never reached.
-    uint32_t pub = arrived >> 16;
-    for (int spin = 0; pub + 1u < nl && spin < (1 << 22); ++spin) {
-        __builtin_amdgcn_s_sleep(2);
-        pub = first_u32(__hip_atomic_load(ticket_of(a, b), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) >> 16;
-    }
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    done = true;
-    return kept;
+    return ns;
 }
 
-// The last workgroup of batch element b to arrive merges its own list (in
-// LDS, `best`, `kept` keys) with the lists every other workgroup published.
-template <bool BIGK>
-__device__ __forceinline__ void row_merge(const StepArgs &a, uint64_t *keys, uint64_t *best, uint32_t kept,
-                                          int b, int LG, int lane)
+// The workgroup of batch element b that arrived last at its ticket appends
+// to keys[0..n) the lists the others put in the mailbox. Each of them arrived
+// earlier and fills all k of its slots (kEmptySlot past its list) once its
+// rows are selected; a slot still zero is not there yet, and is read again.
+// A wait that exceeds the poll limit gives up (`failed`). Returns the new
+// count.
+__device__ __forceinline__ uint32_t take_lists(const StepArgs &a, uint64_t *keys, uint32_t n, int b, int nl,
+                                               int self, int lane, bool &failed)
 {
-    const int C = a.chunks, beam = a.beam, k = a.k;
-    const int Lf = (int)mdiv((uint32_t)b * (uint32_t)(beam * C), a.mw);
-    const int Ll = (int)mdiv(((uint32_t)b + 1) * (uint32_t)(beam * C) - 1, a.mw);
-    const int nl = Ll - Lf + 1, self = LG - Lf;
-    const uint64_t *lists = a.slots + (long long)b * a.maxl * k;
-    const uint64_t *counts = a.head + (long long)b * a.maxl;
-    if ((uint32_t)lane < kept)
-        keys[lane] = best[lane];
-    uint32_t n = kept;
-    for (int g0 = 0; g0 < nl * k; g0 += kLanes) {
+    const int k = a.k, nslot = nl * k;
+    const uint64_t *box = a.mailbox + (long long)b * a.maxl * k;
+    const float invk = 1.f / (float)k;
+    for (int g0 = 0; g0 < nslot && !failed; g0 += kLanes) {
         const int gi = g0 + lane;
-        const int li = gi < nl * k ? gi / k : 0;
-        const bool rd = gi < nl * k && li != self;
-        const uint64_t ent = rd ? get64(&lists[gi]) : 0ull;
-        const uint64_t cnt = rd ? get64(&counts[li]) : 0ull;
-        const bool ok = rd && (uint64_t)(gi - li * k) < cnt;
+        const bool rd = gi < nslot && small_div(gi, invk) != self;
+        uint64_t ent = kEmptySlot;
+        for (unsigned spin = 0;; ++spin) { // uniform
+            if (spin >= a.spin_limit) {
+                failed = true;
+                break;
+            }
+            ent = rd ? get64(&box[gi]) : kEmptySlot;
+            if (ballot(ent == 0) == 0)
+                break;
+            __builtin_amdgcn_s_sleep(2);
+        }
+        const bool ok = !failed && ent != kEmptySlot;
         const uint64_t mk = ballot(ok);
         if (ok)
             keys[n + lane_prefix(mk)] = ent;
         n += (uint32_t)__builtin_popcountll(mk);
     }
-    wave_sync();
-    const uint32_t nk = wave_topk<BIGK>(keys, n, k, lane, best);
-    finish_outputs<BIGK>(a, b, best, nk, lane);
-    if (lane == 0)
-        put32(ticket_of(a, b), 0u);
+    return n;
+}
+
+// Wave 0 of a row-local workgroup, once every piece of it is done, for each
+// batch element b of its rows: the candidates of its rows; if b has rows in
+// other workgroups, either this workgroup arrived last at b's ticket and
+// appends the others' lists, or it leaves its own k best in the mailbox; then
+// the k best of the keys, and the outputs of b from the one that merges.
+// Every mailbox slot read and the ticket go back to zero. A merge whose wait
+// gave up writes padding and sets status word 0 (the fixed region must then
+// be cleared before the next call).
+template <bool BIGK>
+__device__ __forceinline__ void rl_tail(const StepArgs &a, const SelectLds *wl, uint64_t *keys, uint64_t *best,
+                                        uint32_t ufirst, int LG, int bfirst, int blast, int rfirst, int rlast,
+                                        int lane)
+{
+    const int PB = a.beam * a.chunks; // pieces of a batch element
+    // The arrival at the ticket of each batch element that also has rows in
+    // other workgroups (lane i for bfirst + i), counted once every piece of
+    // this workgroup is done: the last workgroup to arrive merges, and every
+    // other one has its list ready by then or soon. The round trip overlaps
+    // the candidate selection below.
+    uint32_t arrived = 0;
+    {
+        const int bb = bfirst + lane;
+        if (bb <= blast && (bb * a.beam < rfirst || (bb + 1) * a.beam - 1 > rlast))
+            arrived = __hip_atomic_fetch_add(ticket_of(a, bb), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    for (int b = bfirst; b <= blast; ++b) {
+        const int j0 = rfirst > b * a.beam ? rfirst - b * a.beam : 0;
+        const int j1 = rlast < (b + 1) * a.beam - 1 ? rlast - b * a.beam : a.beam - 1;
+        const bool whole = j0 == 0 && j1 == a.beam - 1; // every row of b is here
+        int nl = 1, self = 0;
+        bool merge = true;
+        if (!whole) {
+            const int Lf = (int)mdiv((uint32_t)b * (uint32_t)PB, a.mw);
+            const int Ll = (int)mdiv(((uint32_t)b + 1) * (uint32_t)PB - 1, a.mw);
+            nl = Ll - Lf + 1; // workgroups holding rows of b
+            self = LG - Lf;
+        }
+        uint32_t n = row_candidates(a, wl, keys, ufirst, b, j0, j1, lane);
+        if (!whole)
+            merge = first_u32(__builtin_amdgcn_readlane(arrived, b - bfirst)) + 1 >= (uint32_t)nl;
+        bool failed = false;
+        if (!whole && merge)
+            n = take_lists(a, keys, n, b, nl, self, lane, failed);
+        wave_sync();
+        const uint32_t kept = failed ? 0u : wave_topk<BIGK>(keys, n, a.k, lane, best);
+        if (merge) {
+            finish_outputs<BIGK>(a, b, best, kept, lane);
+            if (failed) {
+                if (lane == 0)
+                    __hip_atomic_fetch_or(&a.status[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            } else if (!whole) {
+                uint64_t *box = a.mailbox + (long long)b * a.maxl * a.k;
+                const float invk = 1.f / (float)a.k;
+                for (int gi = lane; gi < nl * a.k; gi += kLanes)
+                    if (small_div(gi, invk) != self)
+                        put64(&box[gi], 0ull);
+                if (lane == 0)
+                    put32(ticket_of(a, b), 0u);
+            }
+        } else { // hand the list over (all k slots, kEmptySlot past it)
+            uint64_t *box = a.mailbox + ((long long)b * a.maxl + self) * a.k;
+            for (int p = lane; p < a.k; p += kLanes)
+                put64(&box[p], (uint32_t)p < kept ? best[p] : kEmptySlot);
+        }
+        wave_sync();
+    }
 }
 
 // Per-piece publication: tickets count the pieces; the workgroup that
@@ -1837,34 +1903,24 @@ __device__ __forceinline__ void rtopk_step_tail(const StepArgs &a, GroupLds &g, 
     const int P = a.beam * a.chunks;
     const int bfirst = (int)mdiv(ufirst, a.mp), blast = (int)mdiv(ulast, a.mp); // at most W batch elements
     if (wave == 0) {
-        // A ticket counts pieces in its low 20 bits and, above them, the
-        // arrivals from workgroups that did not run on the XCD expected for
-        // the batch element: if there were none, every piece of it was
-        // published through one L2 (that of the completing workgroup).
         const int bb = bfirst + lane;
-        bool done = false, local = false;
+        bool done = false;
         if (bb <= blast) {
             const long long lo = (long long)bb * P > ufirst ? (long long)bb * P : ufirst;
             const long long hi = (long long)(bb + 1) * P - 1 < ulast ? (long long)(bb + 1) * P - 1 : ulast;
             const uint32_t n = (uint32_t)(hi - lo + 1);
-            const int xb = xcd_of_logical((int)mdiv((uint32_t)bb * (uint32_t)P, a.mw), (int)gridDim.x);
-            const uint32_t inc = n + ((xcc_id() != (uint32_t)xb ? 1u : 0u) << 20);
             const uint32_t now =
-                __hip_atomic_fetch_add(ticket_of(a, bb), inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + inc;
-            done = (now & 0xfffffu) == (uint32_t)P; // every piece of bb has published
-            local = done && (now >> 20) == 0;
+                __hip_atomic_fetch_add(ticket_of(a, bb), n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + n;
+            done = now == (uint32_t)P; // every piece of bb has published
         }
-        const uint64_t m = ballot(done), ml = ballot(local);
+        const uint64_t m = ballot(done);
         if (lane == 0) {
             g.todo[0] = (uint32_t)m;
             g.todo[1] = (uint32_t)(m >> 32);
-            g.local[0] = (uint32_t)ml;
-            g.local[1] = (uint32_t)(ml >> 32);
         }
     }
     lds_barrier();
     uint64_t todo = ((uint64_t)g.todo[1] << 32) | g.todo[0];
-    const uint64_t local = ((uint64_t)g.local[1] << 32) | g.local[0];
     if (todo == 0)
         return;
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -1886,7 +1942,7 @@ __device__ __forceinline__ void rtopk_step_tail(const StepArgs &a, GroupLds &g, 
             group_sync(SW); // the previous batch element's LDS readers are done
         again = true;
         if (SW == 1)
-            sort_batch_wave(a, sm, bfirst + i, lane, (local >> i) & 1);
+            sort_batch_wave(a, sm, bfirst + i, lane);
         else
             sort_batch(a, sm, g, bfirst + i, tid, SW);
     }
@@ -1907,6 +1963,7 @@ __global__ __launch_bounds__(kLanes *kMaxWaves) void rtopk_step(const StepArgs a
     const int LG = logical_group((int)blockIdx.x, (int)gridDim.x);
     const uint32_t ufirst = (uint32_t)LG * (uint32_t)W;
     const uint32_t u = ufirst + (uint32_t)wave;
+    const uint32_t ulast = (ufirst + W < total ? ufirst + W : total) - 1;
     const uint32_t row0 = mdiv(ufirst, a.mc);
     uint32_t *gshare = reinterpret_cast<uint32_t *>(lds + kLdsShare);
     // The barrier before the loads orders the clearing of the shared group
@@ -1915,33 +1972,28 @@ __global__ __launch_bounds__(kLanes *kMaxWaves) void rtopk_step(const StepArgs a
     for (int i = tid; i < W * kMaxK; i += kLanes * W)
         gshare[i] = 0x007fffffu; // ord_bits(-inf)
     lds_barrier();
-    select_piece<DT, NV, ALIGNED ? kAligned : kGeneral, (RL > 0)>(
-        a, *reinterpret_cast<SelectLds *>(lds + hdr + wave * sizeof(SelectLds)), gshare, u, u < total, row0, lane);
 
-    // Every wave has drained its stores. A workgroup's resources are released
-    // only when its last wave ends, so the others wait here for free; wave 0
-    // then reports the workgroup's pieces to the tickets of their batch
-    // elements, and the workgroup selects the outputs of any it completed.
-    lds_barrier();
-    const uint32_t ulast = (ufirst + W < total ? ufirst + W : total) - 1;
+    const int rfirst = (int)row0, rlast = (int)mdiv(ulast, a.mc);
+    Piece<NV> P;
+    piece_load<DT, NV, (RL > 0)>(a, P, gshare, u, u < total, row0, lane);
+    SelectLds &sm = *reinterpret_cast<SelectLds *>(lds + hdr + wave * sizeof(SelectLds));
+    constexpr int MODE = ALIGNED ? kAligned : kGeneral;
     if constexpr (RL > 0) {
+        piece_compute<DT, NV, MODE, true>(a, sm, P, u, lane);
+        // Every wave is done with its piece. A workgroup's resources are
+        // released only when its last wave ends, so the others wait here for
+        // free; then wave 0 selects what the workgroup holds.
+        lds_barrier();
         if (wave != 0)
             return;
         const SelectLds *wl = reinterpret_cast<const SelectLds *>(lds + hdr);
         uint64_t *keys = reinterpret_cast<uint64_t *>(lds + hdr + (size_t)W * sizeof(SelectLds));
         uint64_t *best = keys + rowlocal_keys(W, a.k, a.maxl);
-        const int rfirst = (int)row0, rlast = (int)mdiv(ulast, a.mc);
-        const int blast = (int)mdiv((uint32_t)rlast, a.mb);
-        for (int b = (int)mdiv((uint32_t)rfirst, a.mb); b <= blast; ++b) {
-            const int j0 = rfirst > b * a.beam ? rfirst - b * a.beam : 0;
-            const int j1 = rlast < (b + 1) * a.beam - 1 ? rlast - b * a.beam : a.beam - 1;
-            bool done;
-            const uint32_t kept = row_select<(RL > 1)>(a, wl, keys, best, ufirst, LG, b, j0, j1, lane, done);
-            if (done)
-                row_merge<(RL > 1)>(a, keys, best, kept, b, LG, lane);
-            wave_sync();
-        }
+        rl_tail<(RL > 1)>(a, wl, keys, best, ufirst, LG, (int)mdiv((uint32_t)rfirst, a.mb),
+                          (int)mdiv((uint32_t)rlast, a.mb), rfirst, rlast, lane);
     } else {
+        piece_compute<DT, NV, MODE, false>(a, sm, P, u, lane);
+        lds_barrier();
         rtopk_step_tail(a, g, lds, hdr, tid, lane, wave, W, ufirst, ulast);
     }
 }

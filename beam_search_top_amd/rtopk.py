@@ -18,9 +18,12 @@ LIB_PATH = os.path.join(_PKG, "librtopk.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "rtopk.h")
 
 RTOPK_F32, RTOPK_F16, RTOPK_BF16 = 0, 1, 2
-RTOPK_OK, RTOPK_EINVAL, RTOPK_ENOTSUP, RTOPK_ENOMEM, RTOPK_EHIP = 0, -1, -2, -3, -4
+RTOPK_OK, RTOPK_EINVAL, RTOPK_ENOTSUP, RTOPK_ENOMEM, RTOPK_EHIP, RTOPK_ETIMEOUT = 0, -1, -2, -3, -4, -5
 RTOPK_MAX_K, RTOPK_MAX_BEAM = 64, 512
-STATUS_NAMES = {0: "RTOPK_OK", -1: "RTOPK_EINVAL", -2: "RTOPK_ENOTSUP", -3: "RTOPK_ENOMEM", -4: "RTOPK_EHIP"}
+RTOPK_WS_FIXED_BYTES = 1310976
+RTOPK_DEFAULT_SPIN_LIMIT = 1 << 22
+STATUS_NAMES = {0: "RTOPK_OK", -1: "RTOPK_EINVAL", -2: "RTOPK_ENOTSUP", -3: "RTOPK_ENOMEM", -4: "RTOPK_EHIP",
+                -5: "RTOPK_ETIMEOUT"}
 
 
 class RtopkError(RuntimeError):
@@ -67,6 +70,12 @@ def load():
     L.rtopk_set_override.restype = i32
     L.rtopk_set_row_local.argtypes = [i32]
     L.rtopk_set_row_local.restype = i32
+    L.rtopk_set_waves.argtypes = [i32]
+    L.rtopk_set_waves.restype = i32
+    L.rtopk_set_spin_limit.argtypes = [ctypes.c_uint]
+    L.rtopk_set_spin_limit.restype = i32
+    L.rtopk_check.argtypes = [vp, vp]
+    L.rtopk_check.restype = i32
     L.rtopk_beam_step_sharded.argtypes = [ctypes.POINTER(vp), i32, i32, vp, vp, i32, i32, i32, i32, i32,
                                           vp, vp, vp, vp]
     L.rtopk_beam_step_sharded.restype = i32
@@ -130,6 +139,18 @@ def rtopk_set_override(vecs_per_thread, chunk_limit):
 
 def rtopk_set_row_local(enable):
     return load().rtopk_set_row_local(enable)
+
+
+def rtopk_set_waves(waves):
+    return load().rtopk_set_waves(waves)
+
+
+def rtopk_set_spin_limit(polls):
+    return load().rtopk_set_spin_limit(polls)
+
+
+def rtopk_check(workspace, stream):
+    return load().rtopk_check(workspace, stream)
 
 
 def rtopk_beam_step_sharded(shards, dtype, alive_scores, finished_mask, B, beam, V_shard, k, eos_id,

@@ -63,7 +63,8 @@ typedef enum {
     RTOPK_ENOTSUP = -2, /* valid but beyond the implementation limits: k > 64, beam > 512,
                            B > 65536, beam * pieces-per-row > 3072 */
     RTOPK_ENOMEM = -3,  /* device allocation failed, or a caller workspace is too small */
-    RTOPK_EHIP = -4     /* a HIP runtime call or kernel launch failed */
+    RTOPK_EHIP = -4,    /* a HIP runtime call or kernel launch failed */
+    RTOPK_ETIMEOUT = -5 /* reported by rtopk_check: a cross-workgroup wait of an earlier call gave up */
 } rtopk_status;
 
 /* Implementation limits. */
@@ -88,7 +89,9 @@ typedef enum {
  * `lds_bytes` is the dynamic LDS of one workgroup. When `row_local` is set
  * (chunks divides pieces_per_group), workgroups hold whole rows: each selects
  * the exact top-k of the rows it holds in LDS, and only those lists of k
- * keys are exchanged between the workgroups that share a batch element.
+ * keys are exchanged between the workgroups that share a batch element (the
+ * last of them to start merges; the others leave their lists in the
+ * workspace's mailbox).
  */
 typedef struct {
     int chunks;          /* pieces per beam row (C) */
@@ -155,11 +158,13 @@ size_t rtopk_workspace_bytes(int B, int beam, int V, int k, int dtype);
  * rtopk_beam_step with a caller-owned device workspace of ws_bytes >=
  * rtopk_workspace_bytes(...) bytes, 256-byte aligned. It must be zero-filled
  * before its first use; every completed call leaves it ready for any later
- * call whose shape fits (its first 256 KiB, the arrival counters, are zero
- * again after each call; the rest holds scratch data). Calls sharing one
- * workspace must be ordered (same stream). Allocates nothing. RTOPK_ENOMEM
- * when ws_bytes is too small.
+ * call whose shape fits (its first RTOPK_WS_FIXED_BYTES bytes -- arrival
+ * counters, status words and the mailbox through which workgroups hand over
+ * their lists -- are zero again after each call; the rest holds scratch
+ * data). Calls sharing one workspace must be ordered (same stream).
+ * Allocates nothing. RTOPK_ENOMEM when ws_bytes is too small.
  */
+#define RTOPK_WS_FIXED_BYTES 1310976
 int rtopk_beam_step_ws(const void *logits, int dtype, const float *alive_scores,
                        const uint8_t *finished_mask, int B, int beam, int V, int k, int eos_id,
                        int32_t *out_beam_ids, int32_t *out_token_ids, float *out_scores,
@@ -199,6 +204,37 @@ int rtopk_plan(const void *logits, int B, int beam, int V, int k, int dtype, rto
  * candidates.
  */
 int rtopk_set_override(int vecs_per_thread, int chunk_limit);
+
+/*
+ * Process-wide tuning override for experiments and tests: the pieces (waves)
+ * per workgroup, 1..16, or 0 for the planner's choice (RTOPK_EINVAL outside
+ * 0..16). Shapes whose pieces per row do not divide it take the per-piece
+ * publication path.
+ */
+int rtopk_set_waves(int waves);
+
+/*
+ * Process-wide bound of the one wait in the selection kernel: the workgroup
+ * that merges a batch element whose rows span several workgroups polls the
+ * others' lists at most `polls` times (default 4194304, each poll followed
+ * by a short sleep) before it gives up. The other workgroups are running
+ * when the wait starts (they counted their arrival before it), so the bound
+ * is only reached if the GPU stops running them, e.g. under preemption. On
+ * give-up the batch element's outputs are written as padding (-1, -1, -inf)
+ * and the workspace's status word is set; rtopk_check reports it. 0 gives up
+ * without polling (tests use it to exercise that path). Always RTOPK_OK.
+ */
+int rtopk_set_spin_limit(unsigned polls);
+
+/*
+ * Synchronises `stream` and reports whether a wait of an earlier call on
+ * `workspace` (a caller workspace of rtopk_beam_step_ws / rtopk_debug_step,
+ * or NULL for the library-owned workspace of `stream`) gave up:
+ * RTOPK_ETIMEOUT, after clearing the workspace's fixed region so that later
+ * calls are exact again (those batch elements were written as padding).
+ * RTOPK_OK when no wait gave up, RTOPK_EHIP when a HIP call fails.
+ */
+int rtopk_check(void *workspace, void *stream);
 
 /*
  * Process-wide switch for tests and experiments: 0 turns the row-local

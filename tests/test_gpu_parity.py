@@ -256,18 +256,61 @@ def test_library_workspace_survives_shape_changes():
 
 
 def test_caller_workspace_tickets_return_to_zero():
-    # Only the arrival counters (the first 256 KiB) must be zero between calls;
-    # calls of different shapes then share one caller workspace.
+    # Only the fixed region (arrival counters, status words, mailbox) must be
+    # zero between calls; calls of different shapes then share one caller
+    # workspace (row-local and per-piece shapes alternate here).
     s_small = synth.make_custom(3, 4, 4, 40000, synth.F16, seed=31, n_finished=1)
     s_big = synth.make_step("b128")
     nbytes = rtopk.rtopk_workspace_bytes(s_big.B, s_big.beam, s_big.V, s_big.k, s_big.dtype)
     ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
-    for s in (s_small, s_big, s_small, s_big):
+    s_pub = synth.make_custom(2, 3, 3, 20001, synth.F16, seed=32, n_finished=1)
+    st, p = rtopk.rtopk_plan(None, s_pub.B, s_pub.beam, s_pub.V, s_pub.k, s_pub.dtype)
+    assert st == 0 and p.row_local == 0
+    nbytes = max(nbytes, rtopk.rtopk_workspace_bytes(s_pub.B, s_pub.beam, s_pub.V, s_pub.k, s_pub.dtype))
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
+    for s in (s_small, s_big, s_pub, s_small, s_big, s_pub, s_big):
         x, a, f = to_device(s)
         out = rtopk.beam_step(x, a, f, k=s.k, workspace=ws)
         torch.cuda.synchronize()
-        assert int(torch.count_nonzero(ws[:256 * 1024])) == 0
+        assert int(torch.count_nonzero(ws[:rtopk.RTOPK_WS_FIXED_BYTES])) == 0
         check(s, [o.cpu().numpy() for o in out])
+
+
+def test_wait_give_up_is_reported_and_cleared():
+    # The merge of a batch element whose rows span workgroups waits for the
+    # others' lists with a bounded poll. A bound of 0 makes every such merge
+    # give up at once (no kernel waits or faults): its outputs are padding,
+    # rtopk_check reports RTOPK_ETIMEOUT and clears the workspace, and the
+    # next call is exact again.
+    s = synth.make_step("b128")
+    st, p = rtopk.rtopk_plan(None, s.B, s.beam, s.V, s.k, s.dtype)
+    assert st == 0 and p.row_local == 1 and p.pieces_per_group < s.beam * p.chunks  # rows span workgroups
+    x, a, f = to_device(s)
+    stream = torch.cuda.current_stream().cuda_stream
+    for use_ws in (False, True):
+        ws = None
+        if use_ws:
+            ws = torch.zeros(rtopk.rtopk_workspace_bytes(s.B, s.beam, s.V, s.k, s.dtype), dtype=torch.uint8,
+                             device=DEV)
+        wsp = None if ws is None else ws.data_ptr()
+        rtopk.beam_step(x, a, f, k=s.k, workspace=ws)
+        assert rtopk.rtopk_check(wsp, stream) == rtopk.RTOPK_OK
+        assert rtopk.rtopk_set_spin_limit(0) == 0
+        try:
+            out = rtopk.beam_step(x, a, f, k=s.k, workspace=ws)
+            torch.cuda.synchronize()
+        finally:
+            rtopk.rtopk_set_spin_limit(rtopk.RTOPK_DEFAULT_SPIN_LIMIT)
+        assert (out[0] == -1).all() and (out[1] == -1).all() and torch.isneginf(out[2]).all()
+        assert rtopk.rtopk_check(wsp, stream) == rtopk.RTOPK_ETIMEOUT
+        assert "gave up" in rtopk.rtopk_last_error()
+        assert rtopk.rtopk_check(wsp, stream) == rtopk.RTOPK_OK  # cleared
+        if ws is not None:
+            assert int(torch.count_nonzero(ws[:rtopk.RTOPK_WS_FIXED_BYTES])) == 0
+        out = rtopk.beam_step(x, a, f, k=s.k, workspace=ws)
+        torch.cuda.synchronize()
+        check(s, [o.cpu().numpy() for o in out])
+        assert rtopk.rtopk_check(wsp, stream) == rtopk.RTOPK_OK
 
 
 def test_candidate_scoring_exactly_at_the_bound():
