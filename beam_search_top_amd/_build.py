@@ -32,6 +32,7 @@ KERNELS = os.path.join(CSRC, "rtopk_kernels.hip")
 HOST = os.path.join(CSRC, "rtopk_host.cpp")
 REORDER = os.path.join(CSRC, "rtopk_reorder.hip")
 SAMPLE = os.path.join(CSRC, "rtopk_sample.hip")
+NOALLOC = os.path.join(CSRC, "rtopk_noalloc.hip")
 DTYPES = (0, 1, 2)  # the kernel source is compiled once per logit type, in parallel
 
 
@@ -53,9 +54,10 @@ def _run(cmds, verbose):
 
 def build(verbose: bool = False, extra=()) -> str:
     tag = f".tmp{os.getpid()}"
-    objs = [LIB + f".dt{d}{tag}.o" for d in DTYPES] + [LIB + f".sample{tag}.o", LIB + f".reorder{tag}.o",
-                                                       LIB + f".host{tag}.o"]
+    objs = [LIB + f".dt{d}{tag}.o" for d in DTYPES] + [LIB + f".noalloc{tag}.o", LIB + f".sample{tag}.o",
+                                                       LIB + f".reorder{tag}.o", LIB + f".host{tag}.o"]
     cmds = [[HIPCC, *FLAGS, *extra, f"-DRTOPK_DTYPE={d}", "-c", KERNELS, "-o", o] for d, o in zip(DTYPES, objs)]
+    cmds.append([HIPCC, *FLAGS, *extra, "-c", NOALLOC, "-o", objs[-4]])
     cmds.append([HIPCC, *FLAGS, *extra, "-c", SAMPLE, "-o", objs[-3]])
     cmds.append([HIPCC, *FLAGS, *extra, "-c", REORDER, "-o", objs[-2]])
     cmds.append([HIPCC, *FLAGS, *extra, "-c", HOST, "-o", objs[-1]])

@@ -27,15 +27,21 @@ namespace {
 
 thread_local std::string g_err;
 
-int fail(int status, const char *fmt, ...)
+int vfail(int status, const char *fmt, va_list ap)
 {
     char buf[512];
-    va_list ap;
-    va_start(ap, fmt);
     vsnprintf(buf, sizeof buf, fmt, ap);
-    va_end(ap);
     g_err = buf;
     return status;
+}
+
+int fail(int status, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    const int st = vfail(status, fmt, ap);
+    va_end(ap);
+    return st;
 }
 
 std::atomic<int> g_override_nv{0};
@@ -392,6 +398,15 @@ int acquire_zeros(size_t n, hipStream_t stream, const float **out)
 
 } // namespace
 
+int rtopk::set_error(int status, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    const int st = vfail(status, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
 extern "C" {
 
 int rtopk_beam_step(const void *logits, int dtype, const float *alive_scores,
@@ -567,35 +582,49 @@ int rtopk_set_spin_limit(unsigned polls)
     return RTOPK_OK;
 }
 
+// Reads the status word of workspace `ws`; if a wait gave up, clears the
+// fixed region (late lists may have landed in the mailbox after the call).
+int check_workspace(void *ws, hipStream_t stream)
+{
+    uint32_t status = 0;
+    hipError_t e = hipMemcpy(&status, (uint8_t *)ws + rtopk::kWsStatusOff, sizeof status, hipMemcpyDeviceToHost);
+    if (e != hipSuccess)
+        return fail(RTOPK_EHIP, "reading the workspace status: %s", hipGetErrorString(e));
+    if (status == 0)
+        return RTOPK_OK;
+    if ((e = rtopk::launch_zero(ws, rtopk::kWsFixedBytes, stream)) != hipSuccess ||
+        (e = hipStreamSynchronize(stream)) != hipSuccess)
+        return fail(RTOPK_EHIP, "clearing the workspace after a failed wait: %s", hipGetErrorString(e));
+    return fail(RTOPK_ETIMEOUT, "a row-local merge gave up waiting for another workgroup's list (status 0x%x); "
+                "its batch elements were written as padding; the workspace has been cleared", status);
+}
+
 int rtopk_check(void *workspace, void *stream)
 {
     hipError_t e = hipStreamSynchronize((hipStream_t)stream);
     if (e != hipSuccess)
         return fail(RTOPK_EHIP, "hipStreamSynchronize: %s", hipGetErrorString(e));
-    void *ws = workspace;
-    if (!ws) {
-        int dev = 0;
-        if ((e = hipGetDevice(&dev)) != hipSuccess)
-            return fail(RTOPK_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (workspace)
+        return check_workspace(workspace, (hipStream_t)stream);
+    int dev = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess)
+        return fail(RTOPK_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    void *lib = nullptr;
+    {
         std::lock_guard<std::mutex> lock(g_ws_mu);
         auto it = g_ws.find({dev, stream});
-        if (it == g_ws.end() || !it->second.ptr)
-            return RTOPK_OK; // no call has run on this stream
-        ws = it->second.ptr;
+        if (it != g_ws.end())
+            lib = it->second.ptr;
     }
-    uint32_t status = 0;
-    e = hipMemcpy(&status, (uint8_t *)ws + rtopk::kWsStatusOff, sizeof status, hipMemcpyDeviceToHost);
-    if (e != hipSuccess)
-        return fail(RTOPK_EHIP, "reading the workspace status: %s", hipGetErrorString(e));
-    if (status == 0)
-        return RTOPK_OK;
-    // a merge gave up waiting: late lists may have landed in the mailbox after
-    // the call; clear the whole fixed region so the workspace is usable again
-    if ((e = rtopk::launch_zero(ws, rtopk::kWsFixedBytes, (hipStream_t)stream)) != hipSuccess ||
-        (e = hipStreamSynchronize((hipStream_t)stream)) != hipSuccess)
-        return fail(RTOPK_EHIP, "clearing the workspace after a failed wait: %s", hipGetErrorString(e));
-    return fail(RTOPK_ETIMEOUT, "a row-local merge gave up waiting for another workgroup's list (status 0x%x); "
-                "its batch elements were written as padding; the workspace has been cleared", status);
+    int st = RTOPK_OK;
+    if (lib)
+        st = check_workspace(lib, (hipStream_t)stream);
+    if (void *scr = rtopk::noalloc_scratch_if_used(dev)) { // the static scratch of rtopk_beam_step_noalloc
+        const int st2 = check_workspace(scr, (hipStream_t)stream);
+        if (st == RTOPK_OK)
+            st = st2;
+    }
+    return st;
 }
 
 int rtopk_sample_step(const void *logits, int dtype, int R, int V, int k, float temperature, uint64_t seed,

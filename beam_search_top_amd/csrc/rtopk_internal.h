@@ -121,6 +121,11 @@ hipError_t launch_beam_reorder(const void *src, void *dst, long long nslabs, int
                                const int32_t *ids, int ld, hipStream_t stream);
 hipError_t launch_read_probe(const void *src, size_t bytes, uint32_t marker, uint32_t *out, hipStream_t stream);
 
+// The status and thread-local message of the C ABI's last error (rtopk_last_error).
+int set_error(int status, const char *fmt, ...);
+// rtopk_noalloc.hip: the static scratch of device `dev` if a call has used it.
+void *noalloc_scratch_if_used(int dev);
+
 // Templates instantiated for vecs_per_thread.
 bool supported_vecs_per_thread(int nv);
 

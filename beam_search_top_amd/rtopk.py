@@ -21,6 +21,7 @@ RTOPK_F32, RTOPK_F16, RTOPK_BF16 = 0, 1, 2
 RTOPK_OK, RTOPK_EINVAL, RTOPK_ENOTSUP, RTOPK_ENOMEM, RTOPK_EHIP, RTOPK_ETIMEOUT = 0, -1, -2, -3, -4, -5
 RTOPK_MAX_K, RTOPK_MAX_BEAM = 64, 512
 RTOPK_WS_FIXED_BYTES = 1310976
+RTOPK_NOALLOC_SCRATCH_BYTES = 8388608
 RTOPK_DEFAULT_SPIN_LIMIT = 1 << 22
 STATUS_NAMES = {0: "RTOPK_OK", -1: "RTOPK_EINVAL", -2: "RTOPK_ENOTSUP", -3: "RTOPK_ENOMEM", -4: "RTOPK_EHIP",
                 -5: "RTOPK_ETIMEOUT"}
@@ -62,6 +63,8 @@ def load():
     L.rtopk_workspace_bytes.restype = sz
     L.rtopk_beam_step_ws.argtypes = step_args + [vp, sz, vp]
     L.rtopk_beam_step_ws.restype = i32
+    L.rtopk_beam_step_noalloc.argtypes = step_args + [vp]
+    L.rtopk_beam_step_noalloc.restype = i32
     L.rtopk_debug_step.argtypes = step_args + [vp, sz, vp, vp, vp, vp, vp, vp]
     L.rtopk_debug_step.restype = i32
     L.rtopk_plan.argtypes = [vp, i32, i32, i32, i32, i32, ctypes.POINTER(rtopk_plan_t)]
@@ -116,6 +119,12 @@ def rtopk_beam_step_ws(logits, dtype, alive_scores, finished_mask, B, beam, V, k
                        out_beam_ids, out_token_ids, out_scores, workspace, ws_bytes, stream):
     return load().rtopk_beam_step_ws(logits, dtype, alive_scores, finished_mask, B, beam, V, k, eos_id,
                                      out_beam_ids, out_token_ids, out_scores, workspace, ws_bytes, stream)
+
+
+def rtopk_beam_step_noalloc(logits, dtype, alive_scores, finished_mask, B, beam, V, k, eos_id,
+                            out_beam_ids, out_token_ids, out_scores, stream):
+    return load().rtopk_beam_step_noalloc(logits, dtype, alive_scores, finished_mask, B, beam, V, k, eos_id,
+                                          out_beam_ids, out_token_ids, out_scores, stream)
 
 
 def rtopk_debug_step(logits, dtype, alive_scores, finished_mask, B, beam, V, k, eos_id,

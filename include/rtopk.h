@@ -90,8 +90,8 @@ typedef enum {
  * (chunks divides pieces_per_group), workgroups hold whole rows: each selects
  * the exact top-k of the rows it holds in LDS, and only those lists of k
  * keys are exchanged between the workgroups that share a batch element (the
- * last of them to start merges; the others leave their lists in the
- * workspace's mailbox).
+ * last of them to finish its pieces merges; the others leave their lists in
+ * the workspace's mailbox).
  */
 typedef struct {
     int chunks;          /* pieces per beam row (C) */
@@ -171,6 +171,27 @@ int rtopk_beam_step_ws(const void *logits, int dtype, const float *alive_scores,
                        void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * rtopk_beam_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments, the same kernels and results, and no allocation of any
+ * kind (no hipMalloc, no library routine that allocates). Its workspace is a
+ * file-scope device array of RTOPK_NOALLOC_SCRATCH_BYTES (8 MiB) that every
+ * GPU the library runs on holds until the process ends; it is zero when the
+ * library is loaded and every completed call leaves its fixed region zero
+ * again. Every call on one GPU shares that GPU's array: calls that overlap on
+ * one GPU (on different streams) race and must not be made; calls ordered on
+ * one stream are fine. RTOPK_ENOMEM, with nothing launched, when the shape
+ * needs more workspace than the array holds (rtopk_workspace_bytes > 8 MiB);
+ * RTOPK_EHIP when the array's device address cannot be looked up.
+ * rtopk_check(NULL, stream) also reports a give-up of a wait on this array.
+ */
+#define RTOPK_NOALLOC_SCRATCH_BYTES 8388608
+int rtopk_beam_step_noalloc(const void *logits, int dtype, const float *alive_scores,
+                            const uint8_t *finished_mask, int B, int beam, int V, int k, int eos_id,
+                            int32_t *out_beam_ids, int32_t *out_token_ids, float *out_scores,
+                            void *stream);
+
+/*
  * rtopk_beam_step_ws that also copies out intermediate values (for tests):
  *   dbg_T       device [B*beam*chunks] float32: each piece's threshold (-inf if empty)
  *   dbg_hits    device [B*beam*chunks] uint32: logits >= threshold in the piece (its
@@ -229,7 +250,8 @@ int rtopk_set_spin_limit(unsigned polls);
 /*
  * Synchronises `stream` and reports whether a wait of an earlier call on
  * `workspace` (a caller workspace of rtopk_beam_step_ws / rtopk_debug_step,
- * or NULL for the library-owned workspace of `stream`) gave up:
+ * or NULL for the library-owned workspace of `stream` and the static scratch
+ * of rtopk_beam_step_noalloc on the current device) gave up:
  * RTOPK_ETIMEOUT, after clearing the workspace's fixed region so that later
  * calls are exact again (those batch elements were written as padding).
  * RTOPK_OK when no wait gave up, RTOPK_EHIP when a HIP call fails.
