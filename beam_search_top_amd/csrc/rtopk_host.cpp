@@ -61,6 +61,7 @@ constexpr long long kTargetGrid = 4096;
 constexpr int kMinVecs = 8;
 // Pieces the GPU runs at once: one 16-wave workgroup per CU on 256 CUs.
 constexpr long long kResidentPieces = 4096;
+constexpr long long kCUs = 256;
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -176,6 +177,19 @@ int make_plan(const void *logits, int B, int beam, int V, int k, int dtype, rtop
     // workgroups (measured: 512 rows x 40000 fp16, k = 40, 57 -> 39 us).
     if (g_rowlocal.load() && k >= 16 && p->waves % C == 0 && (long long)beam * C < p->waves)
         p->waves = (int)(beam * C);
+    // A small row-local grid (fewer workgroups than CUs) takes smaller
+    // workgroups: the smallest that holds whole batch elements when one fits
+    // (no handoff between workgroups), else one row per workgroup, which
+    // spreads the stream over more CUs (measured: 32 x 4 x 40000 fp16 12.4 ->
+    // 10.1 us with 8-wave workgroups; 2 x 2 x 8 fp32 5.4 -> 4.1 us with 2).
+    else if (g_rowlocal.load() && p->waves % C == 0 && ceil_div(rows * C, p->waves) < kCUs) {
+        const long long whole = (long long)beam * C;
+        int w = (int)C;
+        if (whole <= p->waves)
+            while (w < whole)
+                w <<= 1;
+        p->waves = w;
+    }
     // Row-local: when a row's pieces divide the workgroup, workgroups hold
     // whole rows and select them themselves; a batch element's rows then span
     // at most maxl workgroups, which exchange one list of k keys each.

@@ -200,3 +200,16 @@ def test_binding_rejects_host_logits():
     a = torch.zeros((2, 3), dtype=torch.float32)
     with pytest.raises(ValueError):
         rtopk.beam_step(x, a, None, k=2)
+
+
+def test_planner_small_row_local_grids(lib):
+    # fewer row-local workgroups than CUs: whole batch elements per workgroup
+    # when they fit, else one row per workgroup
+    st, p = rtopk.rtopk_plan(None, 2, 2, 8, 2, 0)  # 2 x 2 x 8: one piece per row, batch element = 2 pieces
+    assert st == 0 and p.row_local == 1 and p.pieces_per_group == 2 and p.grid == 2
+    st, p = rtopk.rtopk_plan(None, 32, 4, 40000, 4, 1)  # 8 pieces per row, 32 per batch element
+    assert st == 0 and p.row_local == 1 and p.pieces_per_group == 8 and p.grid == 128
+    st, p = rtopk.rtopk_plan(None, 3, 4, 40000, 4, 1)
+    assert st == 0 and p.row_local == 1 and p.pieces_per_group == 8
+    st, p = rtopk.rtopk_plan(None, 128, 4, 40000, 4, 1)  # a full grid keeps 16-piece workgroups
+    assert st == 0 and p.pieces_per_group == 16 and p.grid == 256

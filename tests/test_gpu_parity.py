@@ -371,7 +371,7 @@ def test_survivors_past_lds_keys_small_k(B, beam, k, V, dt, kw):
 
 @pytest.mark.parametrize("B,beam,k,V,dt,nfin", [
     (16, 4, 12, 40000, synth.F16, 3), (8, 8, 24, 40000, synth.BF16, 4), (6, 2, 9, 40000, synth.F32, 2),
-    (12, 4, 15, 20000, synth.F16, 5),
+    (12, 4, 15, 20000, synth.F16, 5), (256, 2, 12, 40000, synth.F16, 7),
 ])
 def test_row_local_large_k_with_finished_beams(B, beam, k, V, dt, nfin):
     # 8 < k < 16: row-local workgroups may hold rows of several batch elements

@@ -86,7 +86,7 @@ def test_sample_is_reproducible_and_steps_differ():
 
 
 @pytest.mark.parametrize("R,V,k", [(96, 40000, 40), (64, 257, 17), (40, 20000, 64), (96, 40000, 12),
-                                   (50, 30000, 9)])
+                                   (50, 30000, 9), (512, 40000, 12)])
 def test_fused_draw_equals_draw_kernel(R, V, k):
     # row-local k > 8 selections draw in the selection kernel; with row-local
     # selection off the same rows go through the separate draw kernel. Both
