@@ -20,7 +20,7 @@ _SRC = os.path.join(_HERE, "rtopk_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-F32, F16, BF16 = 0, 1, 2
+F32, F16, BF16, F64 = 0, 1, 2, 3
 
 
 def build(force: bool = False) -> str:
@@ -58,6 +58,8 @@ def _configure(L):
     L.rtopk_oracle_decode_f16.restype = f64
     L.rtopk_oracle_decode_bf16.argtypes = [ctypes.c_uint16]
     L.rtopk_oracle_decode_bf16.restype = f64
+    L.rtopk_oracle_lmhead_logits.argtypes = [vp, vp, i64, i64, i64, vp]
+    L.rtopk_oracle_lmhead_logits.restype = None
     return L
 
 
@@ -66,7 +68,7 @@ def _ptr(a):
 
 
 def _logits(x, dtype):
-    want = {F32: np.float32, F16: np.float16, BF16: np.uint16}[dtype]
+    want = {F32: np.float32, F16: np.float16, BF16: np.uint16, F64: np.float64}[dtype]
     x = np.ascontiguousarray(x)
     if x.dtype != want:
         raise TypeError(f"logits dtype {x.dtype} does not match code {dtype}")
@@ -145,6 +147,28 @@ def decode_f16(code: int) -> float:
 
 def decode_bf16(code: int) -> float:
     return _load().rtopk_oracle_decode_bf16(int(code))
+
+
+def lmhead_logits(x_bits, w_bits):
+    """float64 logits [M, V] of the LM head: x [M, H] hidden states and w
+    [V, H] output projection as bfloat16 bit patterns (uint16)."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    w = np.ascontiguousarray(w_bits, dtype=np.uint16)
+    M, H = x.shape
+    V, H2 = w.shape
+    if H != H2:
+        raise ValueError("x and w disagree on H")
+    out = np.empty((M, V), np.float64)
+    _load().rtopk_oracle_lmhead_logits(_ptr(x), _ptr(w), M, V, H, _ptr(out))
+    return out
+
+
+def lmhead_step(x_bits, w_bits, alive, finished, beam, k, eos_id=2, nthreads=1) -> Result:
+    """The fused LM-head step by its definition: the float64 logits of
+    lmhead_logits, then the step oracle on them (rows m = b * beam + j)."""
+    logits = lmhead_logits(x_bits, w_bits)
+    M, V = logits.shape
+    return step(logits.reshape(M // beam, beam, V), F64, alive, finished, k, eos_id, nthreads)
 
 
 def beam_reorder(src, dst_before, beam_ids, nslabs, B, beam):

@@ -41,7 +41,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORACLE_F32 = 0, ORACLE_F16 = 1, ORACLE_BF16 = 2 };
+enum { ORACLE_F32 = 0, ORACLE_F16 = 1, ORACLE_BF16 = 2, ORACLE_F64 = 3 };
 
 /* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
 double rtopk_oracle_decode_f16(uint16_t h)
@@ -70,6 +70,8 @@ double rtopk_oracle_decode_bf16(uint16_t h)
 
 static double load_logit(const void *x, int dtype, int64_t i)
 {
+    if (dtype == ORACLE_F64)
+        return ((const double *)x)[i];
     if (dtype == ORACLE_F32)
         return (double)((const float *)x)[i];
     if (dtype == ORACLE_F16)
@@ -198,7 +200,7 @@ int rtopk_oracle_step(const void *logits, int dtype, const float *alive, const u
         return -1;
     if (B < 1 || beam < 1 || V < 1 || k < 1 || eos_id < 0 || eos_id >= V)
         return -1;
-    if (dtype != ORACLE_F32 && dtype != ORACLE_F16 && dtype != ORACLE_BF16)
+    if (dtype != ORACLE_F32 && dtype != ORACLE_F16 && dtype != ORACLE_BF16 && dtype != ORACLE_F64)
         return -1;
     if (nthreads < 1)
         nthreads = 1;
@@ -311,4 +313,27 @@ int64_t rtopk_oracle_count_ge(const void *logits, int dtype, int64_t base, int64
         if (load_logit(logits, dtype, base + i) >= T)
             c++;
     return c;
+}
+
+/*
+ * The LM head in front of the step: logits[m][v] = sum_h x[m][h] * w[v][h],
+ * x the [M][H] hidden states and w the [V][H] output projection (one row of
+ * H weights per vocabulary entry), both bfloat16 bit patterns. Every product
+ * of two bfloat16 values is exact in float64 and the sum runs in float64 in
+ * h order, so the result is the exact dot product up to float64 rounding of
+ * the sum. The LightSeq inference article computes the logits with a GEMM
+ * ahead of the decoding step and names fusing the operations around GEMMs as
+ * its kernel-fusion principle; this is that GEMM written out, for composing
+ * with rtopk_oracle_step (float64 logits, dtype 3).
+ */
+void rtopk_oracle_lmhead_logits(const uint16_t *x, const uint16_t *w, int64_t M, int64_t V, int64_t H,
+                                double *logits)
+{
+    for (int64_t m = 0; m < M; m++)
+        for (int64_t v = 0; v < V; v++) {
+            double acc = 0.0;
+            for (int64_t h = 0; h < H; h++)
+                acc += rtopk_oracle_decode_bf16(x[m * H + h]) * rtopk_oracle_decode_bf16(w[v * H + h]);
+            logits[m * V + v] = acc;
+        }
 }

@@ -1,4 +1,4 @@
-"""Runs the oracle's pins (tests/test_oracle_pins.py) against another build of
+"""Runs the oracle's pins (tests/test_oracle_pins.py, tests/test_lmhead_cpu.py) against another build of
 the oracle library, given as a path: the planted-mutation check of
 tests/test_oracle_mutants.py starts one process per mutant with this script.
 
@@ -21,9 +21,15 @@ import oracle  # noqa: E402
 
 def main(lib_path):
     oracle._lib = oracle._configure(ctypes.CDLL(lib_path))
-    import test_oracle_pins as pins
+    import test_lmhead_cpu
+    import test_oracle_pins
     from beam_search_top_amd import synth
-    for name, fn in sorted(inspect.getmembers(pins, inspect.isfunction), key=lambda kv: kv[1].__code__.co_firstlineno):
+    fns = []
+    for mod in (test_oracle_pins, test_lmhead_cpu):
+        fns += sorted(inspect.getmembers(mod, inspect.isfunction), key=lambda kv: kv[1].__code__.co_firstlineno)
+    for name, fn in fns:
+        if fn.__module__ not in ("test_oracle_pins", "test_lmhead_cpu"):
+            continue
         if not name.startswith("test_"):
             continue
         args = inspect.signature(fn).parameters

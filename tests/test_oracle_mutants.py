@@ -3,7 +3,7 @@
 Every entry below plants one plausible mistake in a copy of
 oracle/rtopk_oracle.c (a dropped term, a flipped sign, a transposed index, a
 reversed order, an off-by-one, ...), builds that copy with gcc into a
-temporary library and runs the pins of tests/test_oracle_pins.py against it
+temporary library and runs the pins of tests/test_oracle_pins.py and tests/test_lmhead_cpu.py against it
 in a child process (tests/mutant_runner.py). The unchanged source must pass
 the same run. The oracle in the repository is never modified. Only
 mutations that change what the oracle computes belong here (relabelling the
@@ -88,6 +88,15 @@ MUTANTS = [
     ("survivor count with a strict comparison",
      "if (load_logit(logits, dtype, base + i) >= T)",
      "if (load_logit(logits, dtype, base + i) > T)"),
+    ("LM head drops the last hidden unit",
+     "for (int64_t h = 0; h < H; h++)",
+     "for (int64_t h = 0; h < H - 1; h++)"),
+    ("LM head reads the weights transposed",
+     "rtopk_oracle_decode_bf16(w[v * H + h])",
+     "rtopk_oracle_decode_bf16(w[h * V + v])"),
+    ("float64 logits read as float32",
+     "return ((const double *)x)[i];",
+     "return (double)((const float *)x)[i];"),
 ]
 
 
