@@ -110,6 +110,24 @@ struct Plan {
 template <int DT>
 hipError_t launch_dtype(const StepArgs &a, int vecs_per_thread, size_t lds_bytes, hipStream_t stream);
 
+// The LM head fused with pass 1 (rtopk_kernels.hip, bfloat16 unit).
+struct LmArgs {
+    const uint16_t *x;   // [M][H] hidden states, bfloat16 bits
+    const uint16_t *w;   // [V][H] output projection, bfloat16 bits
+    int M, V, H;         // rows (B * beam), vocabulary, hidden size (a multiple of 64)
+    int beam, k, ngroups;
+    int C, mtiles;       // 128-wide vocabulary tiles (pieces per row), 128-row tiles
+    Magic mb;            // division by beam
+    uint64_t *head;      // [M*C][2] piece headers, as the per-piece path publishes them
+    uint64_t *slots;     // [M*C][k] piece top-k keys
+};
+constexpr int kLmTileV = 128;  // vocabulary columns per tile (one piece of a row)
+constexpr int kLmMaxK = 8;     // the epilogue keeps its group maxima in registers
+// Enqueue the tile kernel and the per-batch merge (StepArgs describes the
+// pieces for the merge: chunks = C, head, slots, outputs).
+hipError_t launch_lmhead(const LmArgs &la, const StepArgs &a, size_t merge_lds, hipStream_t stream);
+size_t lmhead_merge_lds(int waves, size_t sort_bytes);
+
 // Enqueue a zero fill of `bytes` (multiple of 4) at `p` (no hipMemsetAsync).
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream);
 // top-k sampling (rtopk_sample.hip)

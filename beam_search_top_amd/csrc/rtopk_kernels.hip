@@ -2030,6 +2030,264 @@ __global__ void zero_fill(uint32_t *p, size_t n)
 }
 #endif
 
+#if RTOPK_DTYPE == 2
+// ------------------------------------------------- LM head fused with pass 1
+// The logits of a decode step come from the LM head, a GEMM:
+// logits[m][v] = sum_h x[m][h] * w[v][h] (hidden states [M][H], output
+// projection [V][H], bfloat16; fp32 accumulation). The LightSeq inference
+// article fuses the work around its GEMMs into them (kernel-fusion passage);
+// here pass 1 and the per-piece top-k of the selection run in the GEMM's
+// epilogue, so the [M][V] logits never reach HBM. Each workgroup computes a
+// 128 x 128 tile with MFMA (v_mfma_f32_32x32x16_bf16; each wave a 64 x 64
+// quarter), then every row of the tile is a piece of the per-piece path: its
+// group maxima (group = vocabulary index mod ngroups), R-top-k threshold,
+// base-2 log-sum-exp partial and exact top-k by (logit desc, flat asc) are
+// published to the workspace, and lmhead_merge selects each batch element.
+constexpr int kLM = 128, kLN = 128, kLK = 64, kLThreads = 256;
+constexpr int kLStride = kLK + 8;  // bf16 per staged LDS row: 144 bytes, 16-byte aligned, spreads the banks
+constexpr int kLHalf = 68;         // floats per half row of the epilogue tile (64 + 4: conflict-free b128 reads)
+constexpr int kLStage = kLM * kLStride * 2; // bytes of one staged 128 x 64 bf16 tile
+constexpr int kLSmem = 4 * kLStage;         // A and B, two stages each (the epilogue tile reuses it)
+static_assert(kLM * 2 * kLHalf * 4 <= kLSmem, "the epilogue tile fits the staging LDS");
+static_assert(kLM * 16 * 8 <= kLSmem, "the per-row candidate lists fit the staging LDS");
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// The 8 best keys seen, descending (0 = empty): insertion by compare-exchange.
+__device__ __forceinline__ void top8_insert(uint64_t (&t)[8], uint64_t key)
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint64_t hi = key > t[i] ? key : t[i];
+        key = key > t[i] ? t[i] : key;
+        t[i] = hi;
+    }
+}
+
+template <int NG>
+__global__ __launch_bounds__(kLThreads) void lmhead_tiles(const LmArgs a)
+{
+    __shared__ __align__(16) uint8_t smem[kLSmem];
+    const int tid = threadIdx.x, lane = tid & (kLanes - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kLanes);
+    const int wm = wave >> 1, wn = wave & 1;
+    // tiles sharing a vocabulary slice are consecutive logical workgroups,
+    // hence on one XCD at about the same time: its weights come from HBM once
+    const int L = logical_group((int)blockIdx.x, (int)gridDim.x);
+    const int nt = L / a.mtiles, mt = L - nt * a.mtiles;
+    const int m0 = mt * kLM, n0 = nt * kLN;
+    // buffer descriptors spanning exactly x and w: rows past M or V read 0
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(a.x), 0, (uint32_t)(a.M * a.H * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(a.w), 0, (uint32_t)(a.V * a.H * 2), 0x00020000);
+    // this thread's 4 + 4 16-byte vectors of a stage: row (tid + 256 i) / 8, vector (tid + 256 i) mod 8
+    uint32_t goff_x[4], goff_w[4], loff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int v = tid + kLThreads * i, r = v >> 3, kv = v & 7;
+        goff_x[i] = (uint32_t)(((m0 + r) * a.H + kv * 8) * 2);
+        goff_w[i] = (uint32_t)(((n0 + r) * a.H + kv * 8) * 2);
+        loff[i] = (uint32_t)((r * kLStride + kv * 8) * 2);
+    }
+    u32x4 gx[4], gw[4];
+    auto load_stage = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            gx[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, goff_x[i] + k0 * 2, 0, 0);
+            gw[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, goff_w[i] + k0 * 2, 0, kBufNT);
+        }
+    };
+    auto store_stage = [&](int st) {
+        uint8_t *A = smem + st * 2 * kLStage, *Bt = A + kLStage;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            *reinterpret_cast<u32x4 *>(A + loff[i]) = gx[i];
+            *reinterpret_cast<u32x4 *>(Bt + loff[i]) = gw[i];
+        }
+    };
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                acc[i][j][e] = 0.f;
+    const int KT = a.H / kLK;
+    load_stage(0);
+    store_stage(0);
+    __syncthreads();
+    // operand rows of this lane: A row (or B column) lane mod 32 of each 32-block,
+    // k values 8 (lane / 32) .. + 7 of each 16-wide step (the same for A and B)
+    const int orow = lane & 31, okoff = (lane >> 5) * 8;
+    for (int kt = 0; kt < KT; ++kt) {
+        const int st = kt & 1;
+        if (kt + 1 < KT)
+            load_stage((kt + 1) * kLK);
+        const uint8_t *A = smem + st * 2 * kLStage, *Bt = A + kLStage;
+#pragma unroll
+        for (int ks = 0; ks < kLK / 16; ++ks) {
+            bf16x8 af[2], bf[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                af[i] = *reinterpret_cast<const bf16x8 *>(
+                    A + ((wm * 64 + i * 32 + orow) * kLStride + ks * 16 + okoff) * 2);
+                bf[i] = *reinterpret_cast<const bf16x8 *>(
+                    Bt + ((wn * 64 + i * 32 + orow) * kLStride + ks * 16 + okoff) * 2);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        }
+        if (kt + 1 < KT)
+            store_stage(st ^ 1);
+        __syncthreads();
+    }
+
+    // ---- the tile to LDS as [row][half][68 floats]: accumulator e of lane l in
+    // block (i, j) is row 32 i + 8 (e / 4) + 4 (l / 32) + e mod 4, column 32 j + l mod 32
+    float *E = reinterpret_cast<float *>(smem);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int r = wm * 64 + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+                const int c = wn * 64 + j * 32 + (lane & 31);
+                E[(r * 2 + (c >> 6)) * kLHalf + (c & 63)] = acc[i][j][e];
+            }
+    __syncthreads();
+
+    // ---- epilogue: thread (row r, half h) holds columns 64 h .. 64 h + 63 of row r
+    const int r = tid >> 1, h = tid & 1;
+    const int gm = m0 + r;          // the row of logits (b * beam + j)
+    const int cbase = n0 + h * 64;  // vocabulary index of this thread's first column
+    const int nvalid = a.V - cbase; // columns of this thread inside the vocabulary (may be <= 0)
+    const float *er = E + (r * 2 + h) * kLHalf;
+    // pass A: group maxima (group = column mod NG; 64 h is a multiple of NG)
+    float gmx[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+        gmx[g] = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const float4 v = *reinterpret_cast<const float4 *>(er + 4 * q);
+        const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int c = 4 * q + e;
+            gmx[c % NG] = c < nvalid ? fmaxf(gmx[c % NG], vv[e]) : gmx[c % NG];
+        }
+    }
+    float rmax = -INFINITY;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        gmx[g] = fmaxf(gmx[g], dpp_f<0xb1>(gmx[g])); // the partner half of the row (lane ^ 1)
+        rmax = fmaxf(rmax, gmx[g]);
+    }
+    // the threshold: the k-th largest of the NG group maxima (the least when k == NG)
+    float srt[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+        srt[g] = gmx[g];
+#pragma unroll
+    for (int i = 0; i < NG; ++i) // descending by exchanges (NG <= 8)
+#pragma unroll
+        for (int j = NG - 1; j > i; --j) {
+            const float hi = fmaxf(srt[j - 1], srt[j]), lo = fminf(srt[j - 1], srt[j]);
+            srt[j - 1] = hi;
+            srt[j] = lo;
+        }
+    float T = srt[0];
+#pragma unroll
+    for (int g = 1; g < NG; ++g)
+        T = g == a.k - 1 ? srt[g] : T;
+    // pass B: the log-sum-exp partial in base 2 around the row maximum, and the candidates
+    const float pm = rmax * kLog2e;
+    const float base = rmax == -INFINITY ? 0.f : pm;
+    float ssum = 0.f;
+    uint64_t cm = 0; // bit c: column c is a candidate (>= T, inside the vocabulary)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const float4 v = *reinterpret_cast<const float4 *>(er + 4 * q);
+        const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int c = 4 * q + e;
+            const bool in = c < nvalid;
+            ssum += in ? fast_exp2(fmaf(vv[e], kLog2e, -base)) : 0.f;
+            cm |= (uint64_t)(in && vv[e] >= T) << c;
+        }
+    }
+    ssum = ssum + dpp_f<0xb1>(ssum);
+    // this half's 8 best candidates by (logit desc, flat asc)
+    const int beamj = gm - (int)mdiv((uint32_t)gm, a.mb) * a.beam;
+    const uint32_t flat0 = (uint32_t)beamj * (uint32_t)a.V + (uint32_t)cbase;
+    uint64_t t8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        t8[i] = 0ull;
+    uint32_t nc = 0;
+    while (cm != 0) {
+        const int c = __builtin_ctzll(cm);
+        cm &= cm - 1;
+        top8_insert(t8, score_key(er[c], flat0 + (uint32_t)c));
+        ++nc;
+    }
+    __syncthreads(); // every thread is done with the tile before the lists replace it
+    // the two halves' lists side by side in LDS, each key ranked against all 16
+    uint64_t *lst = reinterpret_cast<uint64_t *>(smem) + r * 16;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        lst[h * 8 + i] = t8[i];
+    wave_sync(); // both halves of a row are in one wave
+    const uint32_t ntot = nc + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)nc, 0xb1, 0xf, 0xf, false);
+    const uint32_t emit = ntot < (uint32_t)a.k ? ntot : (uint32_t)a.k;
+    if (gm < a.M) { // a row of the tile inside the batch
+        const long long u = (long long)gm * a.C + nt; // the piece (row, tile)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint64_t key = t8[i];
+            if (key == 0ull)
+                continue;
+            uint32_t rank = 0;
+#pragma unroll
+            for (int q = 0; q < 16; ++q)
+                rank += lst[q] > key;
+            if (rank < (uint32_t)a.k)
+                a.slots[u * a.k + rank] = key;
+        }
+        if (h == 0) {
+            a.head[2 * u] = ((uint64_t)__float_as_uint(ssum) << 32) | __float_as_uint(pm);
+            a.head[2 * u + 1] = ((uint64_t)emit << 32) | __float_as_uint(T);
+        }
+    }
+}
+
+// One workgroup per batch element: the per-piece path's selection over the
+// pieces lmhead_tiles published (heads, slots), into the outputs.
+__global__ __launch_bounds__(kLanes *kMaxWaves) void lmhead_merge(const StepArgs a)
+{
+    extern __shared__ __align__(16) uint8_t lds[];
+    GroupLds &g = *reinterpret_cast<GroupLds *>(lds);
+    const int tid = threadIdx.x, lane = tid & (kLanes - 1);
+    const int W = (int)blockDim.x / kLanes;
+    const SortLds sm = sort_lds(lds + lds_header(W), a);
+    const int P = a.beam * a.chunks;
+    if (P <= kLanes && P * a.k <= 4 * kLanes) {
+        if (tid < kLanes)
+            sort_batch_wave(a, sm, (int)blockIdx.x, lane);
+    } else {
+        sort_batch(a, sm, g, (int)blockIdx.x, tid, W);
+    }
+}
+#endif
+
 } // namespace
 
 #if RTOPK_DTYPE == 0
@@ -2077,6 +2335,27 @@ hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream)
     hipLaunchKernelGGL(zero_fill, dim3(blocks), dim3(256), 0, stream, (uint32_t *)p, n);
     return hipGetLastError();
 }
+#endif
+
+#if RTOPK_DTYPE == 2
+hipError_t launch_lmhead(const LmArgs &la, const StepArgs &a, size_t merge_lds, hipStream_t s)
+{
+    const dim3 grid((unsigned)(la.mtiles * la.C)), block(kLThreads);
+    switch (la.ngroups) {
+    case 1: hipLaunchKernelGGL(lmhead_tiles<1>, grid, block, 0, s, la); break;
+    case 2: hipLaunchKernelGGL(lmhead_tiles<2>, grid, block, 0, s, la); break;
+    case 4: hipLaunchKernelGGL(lmhead_tiles<4>, grid, block, 0, s, la); break;
+    case 8: hipLaunchKernelGGL(lmhead_tiles<8>, grid, block, 0, s, la); break;
+    default: return hipErrorInvalidValue;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(lmhead_merge, dim3((unsigned)a.B), dim3(kLanes * a.waves), merge_lds, s, a);
+    return hipGetLastError();
+}
+
+size_t lmhead_merge_lds(int waves, size_t sort_bytes) { return lds_header(waves) + sort_bytes; }
 #endif
 
 template <>

@@ -85,6 +85,8 @@ def load():
     L.rtopk_sample_step.argtypes = [vp, i32, i32, i32, i32, ctypes.c_float, ctypes.c_uint64, ctypes.c_uint64,
                                     vp, vp, vp]
     L.rtopk_sample_step.restype = i32
+    L.rtopk_lmhead_step.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp]
+    L.rtopk_lmhead_step.restype = i32
     L.rtopk_beam_reorder.argtypes = [vp, vp, ctypes.c_longlong, i32, i32, ctypes.c_longlong, vp, i32, vp]
     L.rtopk_beam_reorder.restype = i32
     L.rtopk_read_probe.argtypes = [vp, sz, ctypes.c_uint32, vp, vp]
@@ -211,6 +213,50 @@ def sample_step(logits, k, temperature=1.0, seed=0, step=0):
     _check(rtopk_sample_step(_ptr(logits), dtype_code(logits), R, V, k, float(temperature), int(seed), int(step),
                              _ptr(tok), _ptr(lp), stream))
     return tok, lp
+
+
+def rtopk_lmhead_step(hidden, weight, alive_scores, finished_mask, B, beam, H, V, k, eos_id,
+                      out_beam_ids, out_token_ids, out_scores, stream):
+    return load().rtopk_lmhead_step(hidden, weight, alive_scores, finished_mask, B, beam, H, V, k, eos_id,
+                                    out_beam_ids, out_token_ids, out_scores, stream)
+
+
+def lmhead_step(hidden, weight, alive, finished=None, k=None, eos_id=2):
+    """The step fused into the LM head, on torch device tensors (current
+    stream): hidden [B*beam, H] and weight [V, H] bfloat16, alive [B, beam]
+    float32, finished [B, beam] bool/uint8 or None. Returns (beam_ids,
+    token_ids, scores), each [B, k]."""
+    import torch
+    if hidden.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
+        raise ValueError("hidden and weight must be bfloat16")
+    if hidden.dim() != 2 or weight.dim() != 2 or hidden.shape[1] != weight.shape[1]:
+        raise ValueError("hidden must be [B*beam, H] and weight [V, H]")
+    if not (hidden.is_contiguous() and weight.is_contiguous()) or not hidden.is_cuda:
+        raise ValueError("hidden and weight must be contiguous device tensors")
+    dev = hidden.device
+    _on_device(weight, dev, "weight")
+    _on_device(alive, dev, "alive")
+    if alive.dim() != 2 or alive.dtype != torch.float32 or not alive.is_contiguous():
+        raise ValueError("alive must be a contiguous float32 [B, beam] tensor")
+    B, beam = alive.shape
+    if hidden.shape[0] != B * beam:
+        raise ValueError("hidden must have B*beam rows")
+    if finished is not None:
+        _on_device(finished, dev, "finished")
+        if finished.shape != (B, beam) or finished.dtype not in (torch.uint8, torch.bool):
+            raise ValueError("finished must be a [B, beam] uint8/bool tensor")
+        finished = finished.contiguous()
+        if finished.dtype == torch.bool:
+            finished = finished.view(torch.uint8)
+    if k is None:
+        k = beam
+    V, H = weight.shape
+    outs = (torch.empty((B, k), dtype=torch.int32, device=dev), torch.empty((B, k), dtype=torch.int32, device=dev),
+            torch.empty((B, k), dtype=torch.float32, device=dev))
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    _check(rtopk_lmhead_step(_ptr(hidden), _ptr(weight), _ptr(alive), _ptr(finished), B, beam, H, V, k, eos_id,
+                             _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]), stream))
+    return outs
 
 
 def rtopk_beam_reorder(src, dst, nslabs, B, beam, row_bytes, beam_ids, ld, stream):

@@ -236,6 +236,112 @@ def bench_sample(args):
     print(json.dumps(line), flush=True)
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak
+
+
+def bench_lmhead(args):
+    """The step fused into the LM head (rtopk_lmhead_step): hidden states
+    [B*beam, H] and the [V, H] output projection in bfloat16 for B=128,
+    beam=4, H=1024 (the hidden size of the LightSeq training article's
+    benchmark model), V=40000, k=4, 26 of 512 beams finished; seeded synthetic
+    values (hidden N(0,1), weights N(0, 3/sqrt(H)), so logits are about
+    N(0,3)). The weights rotate through a pool larger than the 256 MB
+    Infinity Cache so every step reads them from HBM. The roofline is the
+    matrix cores' (2 M V H flops per step against the 2.5 PFLOP/s dense bf16
+    peak). For reference the same step unfused is timed too: torch's GEMM
+    (hipBLASLt) writing bf16 logits, then rtopk_beam_step on them."""
+    import numpy as np
+    import torch
+
+    from beam_search_top_amd import rtopk, synth
+    L = rtopk.load()
+    dev = torch.device("cuda:0")
+    B, beam, H, V, k = 128, 4, 1024, 40000, 4
+    M = B * beam
+    rng = np.random.default_rng(1009)
+    x = torch.from_numpy(rng.normal(0, 1, (M, H)).astype(np.float32)).to(dev).to(torch.bfloat16)
+    w0 = torch.from_numpy(rng.normal(0, 3.0 / np.sqrt(H), (V, H)).astype(np.float32)).to(dev).to(torch.bfloat16)
+    nbuf = max(1, math.ceil(args.pool_mib * 2**20 / (V * H * 2)))
+    pool = [w0] + [torch.roll(w0, shifts=7 * i, dims=1).contiguous() for i in range(1, nbuf)]
+    alive = torch.from_numpy(rng.uniform(-30, 0, (B, beam)).astype(np.float32)).to(dev)
+    fin_h = np.zeros(M, np.uint8)
+    fin_h[rng.choice(M, 26, replace=False)] = 1
+    fin = torch.from_numpy(fin_h.reshape(B, beam)).to(dev)
+    ob = torch.empty((B, k), dtype=torch.int32, device=dev)
+    ot = torch.empty_like(ob)
+    osc = torch.empty((B, k), dtype=torch.float32, device=dev)
+    cur = torch.cuda.current_stream()
+
+    def launch(i, stream):
+        rc = L.rtopk_lmhead_step(x.data_ptr(), pool[i % nbuf].data_ptr(), alive.data_ptr(), fin.data_ptr(), B, beam,
+                                 H, V, k, 2, ob.data_ptr(), ot.data_ptr(), osc.data_ptr(), stream)
+        if rc != 0:
+            raise RuntimeError(rtopk.rtopk_last_error())
+
+    for i in range(max(2, min(args.warmup, 20))):
+        launch(i, cur.cuda_stream)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(cur)
+    launch(0, cs.cuda_stream)  # the library workspace of the capture stream exists before capture
+    torch.cuda.synchronize()
+    glen = 20
+    with torch.cuda.graph(graph, stream=cs):
+        for i in range(glen):
+            launch(i, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    K = max(glen, (min(args.steps, 2000) // glen) * glen)
+
+    def timed(fn, n):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(cur)
+        for i in range(n):
+            fn(i)
+        end.record(cur)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / n
+
+    trials = [timed(lambda i: graph.replay(), K // glen) / glen for _ in range(5)]
+    ms = float(np.median(trials))
+    # unfused reference: GEMM to bf16 logits, then the selection on them
+    logits = torch.empty((M, V), dtype=torch.bfloat16, device=dev)
+
+    def unfused(i):
+        torch.matmul(x, pool[i % nbuf].t(), out=logits)
+        rc = L.rtopk_beam_step(logits.data_ptr(), 2, alive.data_ptr(), fin.data_ptr(), B, beam, V, k, 2,
+                               ob.data_ptr(), ot.data_ptr(), osc.data_ptr(), cur.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(rtopk.rtopk_last_error())
+
+    for i in range(5):
+        unfused(i)
+    ms_unfused = float(np.median([timed(unfused, 50) for _ in range(3)]))
+    ms_gemm = float(np.median([timed(lambda i: torch.matmul(x, pool[i % nbuf].t(), out=logits), 50)
+                               for _ in range(3)]))
+    flops = 2.0 * M * V * H
+    tflops = flops / (ms * 1e-3) / 1e12
+    line = {
+        "metric": "LM head fused with the selection step: steps/s and matrix-core TFLOP/s, 1xMI355X",
+        "value": 1e3 / ms, "unit": "beam-steps/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"lmhead_b128: hidden [{M}, {H}] x weight [{V}, {H}] bf16, B={B} beam={beam} k={k}, "
+                               "26/512 beams finished, seed 1009", "B": B, "beam": beam, "H": H, "V": V, "k": k,
+                   "weight_pool_buffers": nbuf},
+        "flops_per_step": flops,
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "traffic": None},
+        "trials_ms": trials,
+        "weight_GBps": V * H * 2 / (ms * 1e-3) / 1e9,
+        "unfused_ms_per_step": ms_unfused,
+        "unfused_gemm_ms": ms_gemm,
+        "unfused": "torch.matmul (hipBLASLt) to bf16 logits [512, 40000], then rtopk_beam_step on them",
+    }
+    print(json.dumps(line), flush=True)
+
+
 def cpu_baseline(s, seconds):
     import oracle
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
@@ -260,9 +366,10 @@ def main():
     ap.add_argument("--config", default="b128")
     ap.add_argument("--shards", type=int, default=1,
                     help="select over G vocabulary shards (rtopk_beam_step_sharded), each its own tensor")
-    ap.add_argument("--path", default="select", choices=["select", "reorder", "sample"],
+    ap.add_argument("--path", default="select", choices=["select", "reorder", "sample", "lmhead"],
                     help="select: the selection step (the default line); reorder: the cache refresh after it; "
-                         "sample: top-k sampling with the same selection")
+                         "sample: top-k sampling with the same selection; lmhead: the step fused into the "
+                         "LM head GEMM")
     ap.add_argument("--launch", default="graph", choices=["graph", "eager"],
                     help="replay the K launches from a captured HIP graph, or launch each from Python")
     ap.add_argument("--pool-mib", type=int, default=1024, help="distinct logit buffers rotated through")
@@ -282,6 +389,9 @@ def main():
         return
     if args.path == "sample":
         bench_sample(args)
+        return
+    if args.path == "lmhead":
+        bench_lmhead(args)
         return
 
     import numpy as np

@@ -291,6 +291,31 @@ int rtopk_sample_step(const void *logits, int dtype, int R, int V, int k, float 
                       uint64_t step, int32_t *out_token, float *out_logprob, void *stream);
 
 /*
+ * The step fused into the LM head in front of it. The LightSeq inference
+ * article computes the logits with a GEMM ahead of the decoding step and
+ * fuses the work around its GEMMs into them (kernel-fusion passage). Here
+ *     logits[b*beam + j][t] = sum_h hidden[b*beam + j][h] * weight[t][h]
+ * (bfloat16 inputs, float32 accumulation on the matrix cores) are computed
+ * in 128 x 128 tiles whose epilogue runs pass 1 and the per-piece top-k of
+ * the selection (a piece = one row of one 128-wide vocabulary tile; its
+ * groups are the vocabulary indices mod ngroups), so the [B*beam][V] logits
+ * never reach HBM; a second launch then selects each batch element exactly
+ * as rtopk_beam_step does. Results are those of rtopk_beam_step on the
+ * float32 logits of that GEMM.
+ *   hidden   device [B*beam][H] bfloat16 (row b*beam + j is beam j of batch element b)
+ *   weight   device [V][H] bfloat16, one row per vocabulary entry (the output
+ *            projection as a [V][H] matrix); both 16-byte aligned
+ *   H        a multiple of 64 (else RTOPK_ENOTSUP)
+ *   k        1 <= k <= min(8, beam*V) (k > 8: RTOPK_ENOTSUP)
+ * Everything else as rtopk_beam_step (library-owned workspace of `stream`).
+ * RTOPK_ENOTSUP also when beam * ceil(V / 128) > 3072 or hidden or weight
+ * spans 2 GiB or more.
+ */
+int rtopk_lmhead_step(const void *hidden, const void *weight, const float *alive_scores,
+                      const uint8_t *finished_mask, int B, int beam, int H, int V, int k, int eos_id,
+                      int32_t *out_beam_ids, int32_t *out_token_ids, float *out_scores, void *stream);
+
+/*
  * Cache refresh after a selection step. The LightSeq inference article's
  * hierarchical-decoding passage ends the step with a cache update once the
  * top-k are known (its profile: 10% of latency in fp32, 6% in fp16). For a
