@@ -707,22 +707,20 @@ int rtopk_lmhead_step(const void *hidden, const void *weight, const float *alive
         return fail(RTOPK_ENOTSUP, "lmhead step: H=%d is not a multiple of 64", H);
     if (k > rtopk::kLmMaxK)
         return fail(RTOPK_ENOTSUP, "lmhead step: k=%d exceeds the fused path's limit %d", k, rtopk::kLmMaxK);
-    if (beam > RTOPK_MAX_BEAM || B > rtopk::kTicketCap)
-        return fail(RTOPK_ENOTSUP, "lmhead step: beam=%d or B=%d beyond the implementation limits", beam, B);
+    if (beam > rtopk::kLmMaxBeam)
+        return fail(RTOPK_ENOTSUP, "lmhead step: beam=%d beyond the implementation limit %d", beam, rtopk::kLmMaxBeam);
     const long long M = (long long)B * beam;
-    if (M * H * 2 >= (1ll << 31) || (long long)V * H * 2 >= (1ll << 31))
+    // buffer offsets are 32-bit, up to the end of the last (partial) tile
+    if ((M + rtopk::kLmTileM) * H * 2 >= (1ll << 31) || ((long long)V + rtopk::kLmTileV) * H * 2 >= (1ll << 31))
         return fail(RTOPK_ENOTSUP, "lmhead step: hidden or weight of 2 GiB or more");
     if ((long long)beam * V > INT_MAX)
         return fail(RTOPK_EINVAL, "lmhead step: beam*V exceeds 2^31-1");
     const long long C = (V + rtopk::kLmTileV - 1) / rtopk::kLmTileV; // pieces per row
-    if ((long long)beam * C > rtopk::kMaxPieces)
-        return fail(RTOPK_ENOTSUP, "lmhead step: beam * ceil(V/128) = %lld exceeds %d", (long long)beam * C,
-                    rtopk::kMaxPieces);
     const long long npieces = M * C;
-    const long long qcap = (long long)beam * C * k;
-    // workspace: the fixed region, then the piece headers and slots
-    const size_t head_off = align256(rtopk::kWsFixedBytes);
-    const size_t slots_off = align256(head_off + 16 * (size_t)npieces);
+    // workspace: the fixed region (left to the step kernels, which share the
+    // cached workspace), then the piece partials and slots
+    const size_t ms_off = align256(rtopk::kWsFixedBytes);
+    const size_t slots_off = align256(ms_off + 8 * (size_t)npieces);
     const size_t need = align256(slots_off + 8 * (size_t)npieces * k);
     void *ws = nullptr;
     int st = acquire_workspace(need, (hipStream_t)stream, &ws);
@@ -732,49 +730,26 @@ int rtopk_lmhead_step(const void *hidden, const void *weight, const float *alive
     rtopk::LmArgs la{};
     la.x = (const uint16_t *)hidden;
     la.w = (const uint16_t *)weight;
+    la.alive = alive_scores;
+    la.finished = finished_mask;
+    la.B = B;
     la.M = (int)M;
     la.V = V;
     la.H = H;
     la.beam = beam;
     la.k = k;
     la.ngroups = pow2_ceil(k);
+    la.eos_id = eos_id;
     la.C = (int)C;
-    la.mtiles = (int)((M + 127) / 128);
+    la.mtiles = (int)((M + rtopk::kLmTileM - 1) / rtopk::kLmTileM);
     la.mb = rtopk::make_magic((uint32_t)beam);
-    la.head = (uint64_t *)(w8 + head_off);
+    la.mv = rtopk::make_magic((uint32_t)V);
+    la.ms = (uint64_t *)(w8 + ms_off);
     la.slots = (uint64_t *)(w8 + slots_off);
-    // the merge reads the pieces as the per-piece path publishes them
-    rtopk::StepArgs a{};
-    a.alive = alive_scores;
-    a.finished = finished_mask;
-    a.B = B;
-    a.beam = beam;
-    a.V = V;
-    a.k = k;
-    a.eos_id = eos_id;
-    a.chunks = (int)C;
-    a.queue_cap = (int)qcap;
-    const long long want_keys = qcap + beam;
-    a.sort_keys = pow2_ceil(want_keys < rtopk::kMaxSortKeys ? (int)want_keys : rtopk::kMaxSortKeys);
-    a.waves = rtopk::kMaxWaves;
-    a.mc = rtopk::make_magic((uint32_t)C);
-    a.mb = la.mb;
-    a.mp = rtopk::make_magic((uint32_t)(beam * C));
-    a.mw = rtopk::make_magic((uint32_t)a.waves);
-    a.mv = rtopk::make_magic((uint32_t)V);
-    a.spin_limit = g_spin_limit.load();
-    a.ticket = (uint32_t *)(w8 + rtopk::kWsTicketOff);
-    a.status = (uint32_t *)(w8 + rtopk::kWsStatusOff);
-    a.mailbox = (uint64_t *)(w8 + rtopk::kWsMailboxOff);
-    a.head = la.head;
-    a.slots = la.slots;
-    a.out_beam = out_beam_ids;
-    a.out_token = out_token_ids;
-    a.out_score = out_scores;
-    const size_t pieces = (size_t)beam * (size_t)C;
-    const size_t sort_lds = 8 * (size_t)a.sort_keys + 13 * pieces + 13 * (size_t)beam;
-    const size_t lds = (rtopk::lmhead_merge_lds(a.waves, sort_lds) + 15) & ~size_t(15);
-    const hipError_t e = rtopk::launch_lmhead(la, a, lds, (hipStream_t)stream);
+    la.out_beam = out_beam_ids;
+    la.out_token = out_token_ids;
+    la.out_score = out_scores;
+    const hipError_t e = rtopk::launch_lmhead(la, (hipStream_t)stream);
     if (e != hipSuccess)
         return fail(RTOPK_EHIP, "lmhead step launch: %s", hipGetErrorString(e));
     return RTOPK_OK;

@@ -114,19 +114,23 @@ hipError_t launch_dtype(const StepArgs &a, int vecs_per_thread, size_t lds_bytes
 struct LmArgs {
     const uint16_t *x;   // [M][H] hidden states, bfloat16 bits
     const uint16_t *w;   // [V][H] output projection, bfloat16 bits
-    int M, V, H;         // rows (B * beam), vocabulary, hidden size (a multiple of 64)
-    int beam, k, ngroups;
-    int C, mtiles;       // 128-wide vocabulary tiles (pieces per row), 128-row tiles
-    Magic mb;            // division by beam
-    uint64_t *head;      // [M*C][2] piece headers, as the per-piece path publishes them
-    uint64_t *slots;     // [M*C][k] piece top-k keys
+    const float *alive;  // [B][beam] running scores
+    const uint8_t *finished; // [B][beam], nonzero = finished; may be null
+    int B, M, V, H;      // batch, rows (B * beam), vocabulary, hidden size (a multiple of 64)
+    int beam, k, ngroups, eos_id;
+    int C, mtiles;       // 320-wide vocabulary tiles (pieces per row), 256-row tiles
+    Magic mb, mv;        // division by beam, by V
+    uint64_t *ms;        // [M*C] piece log-sum-exp partials: sum bits << 32 | max bits (base 2)
+    uint64_t *slots;     // [M*C][k] piece top-k keys by logit, descending, 0 = empty
+    int32_t *out_beam, *out_token;
+    float *out_score;
 };
-constexpr int kLmTileV = 128;  // vocabulary columns per tile (one piece of a row)
+constexpr int kLmTileV = 320;  // vocabulary columns per tile (one piece of a row)
+constexpr int kLmTileM = 256;  // rows per tile
 constexpr int kLmMaxK = 8;     // the epilogue keeps its group maxima in registers
-// Enqueue the tile kernel and the per-batch merge (StepArgs describes the
-// pieces for the merge: chunks = C, head, slots, outputs).
-hipError_t launch_lmhead(const LmArgs &la, const StepArgs &a, size_t merge_lds, hipStream_t stream);
-size_t lmhead_merge_lds(int waves, size_t sort_bytes);
+constexpr int kLmMaxBeam = 512; // rows of a batch element the selection holds in LDS
+// Enqueue the tile kernel and the per-batch selection.
+hipError_t launch_lmhead(const LmArgs &a, hipStream_t stream);
 
 // Enqueue a zero fill of `bytes` (multiple of 4) at `p` (no hipMemsetAsync).
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream);

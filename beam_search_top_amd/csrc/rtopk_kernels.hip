@@ -2037,32 +2037,113 @@ __global__ void zero_fill(uint32_t *p, size_t n)
 // projection [V][H], bfloat16; fp32 accumulation). The LightSeq inference
 // article fuses the work around its GEMMs into them (kernel-fusion passage);
 // here pass 1 and the per-piece top-k of the selection run in the GEMM's
-// epilogue, so the [M][V] logits never reach HBM. Each workgroup computes a
-// 128 x 128 tile with MFMA (v_mfma_f32_32x32x16_bf16; each wave a 64 x 64
-// quarter), then every row of the tile is a piece of the per-piece path: its
-// group maxima (group = vocabulary index mod ngroups), R-top-k threshold,
-// base-2 log-sum-exp partial and exact top-k by (logit desc, flat asc) are
-// published to the workspace, and lmhead_merge selects each batch element.
-constexpr int kLM = 128, kLN = 128, kLK = 64, kLThreads = 256;
-constexpr int kLStride = kLK + 8;  // bf16 per staged LDS row: 144 bytes, 16-byte aligned, spreads the banks
-constexpr int kLHalf = 68;         // floats per half row of the epilogue tile (64 + 4: conflict-free b128 reads)
-constexpr int kLStage = kLM * kLStride * 2; // bytes of one staged 128 x 64 bf16 tile
-constexpr int kLSmem = 4 * kLStage;         // A and B, two stages each (the epilogue tile reuses it)
-static_assert(kLM * 2 * kLHalf * 4 <= kLSmem, "the epilogue tile fits the staging LDS");
-static_assert(kLM * 16 * 8 <= kLSmem, "the per-row candidate lists fit the staging LDS");
+// epilogue, so the [M][V] logits never reach HBM.
+//
+// lmhead_tiles: one workgroup of 8 waves per 256 x 320 tile (rows of x by
+// vocabulary columns). Wave (wm, wn) computes rows 128 wm .. + 127 and
+// columns 80 wn .. + 79 of it as 8 x 5 blocks of v_mfma_f32_16x16x32_bf16
+// (160 accumulator registers). Tall wave tiles keep the LDS bytes read per
+// multiply low, and 256 x 320 tiles cover B*beam = 512 and V = 40000 in 250
+// workgroups, one round on 256 CUs, each reading 256 rows of x and 320 rows
+// of w once. The operands stream through two LDS stages filled by
+// direct-to-LDS buffer loads (no registers in between), 64 steps of H
+// (whole 128-byte lines of every row) per stage, one stage in flight while
+// the other is multiplied. The 8 lanes of a row slice in a load fetch its
+// 16-byte chunks permuted by the row (chunk c of row r at slot c ^ swz(r)),
+// so the fragment reads, 16 rows at one chunk, fall in distinct LDS banks
+// whether the LDS serves 8 or 16 lanes of a 16-byte read per clock. The
+// epilogue then takes the tile 64 rows at a time through LDS, 8 threads per
+// row: every row of the tile is a piece of the per-piece path, whose group
+// maxima (group = vocabulary index mod ngroups), R-top-k threshold, base-2
+// log-sum-exp partial and exact top-k by (logit desc, flat asc) go to the
+// workspace; lmhead_select reduces the pieces of each batch element.
+constexpr int kLM = kLmTileM, kLN = kLmTileV, kLThreads = 512;
+constexpr int kLWaves = kLThreads / kLanes;
+constexpr int kLWM = 128, kLWN = 80;           // rows and columns per wave
+constexpr int kLBI = kLWM / 16, kLBJ = kLWN / 16; // 16 x 16 blocks per wave: 8 x 5
+constexpr int kLK = 64;                        // steps of H per stage
+constexpr int kLStages = 2;
+constexpr int kLRow = kLK * 2;                 // bytes of a row slice (128: one line)
+constexpr int kLRowsLoad = kLanes / (kLRow / 16); // rows per direct load (8)
+constexpr int kLStageA = kLM * kLRow;          // bytes of x in a stage: [256 rows][128 bytes]
+constexpr int kLStage = (kLM + kLN) * kLRow;   // x, then w as [320 rows][128 bytes]
+constexpr int kLSmem = kLStages * kLStage;     // 144 KiB
+constexpr int kLLoadsA = kLM / kLRowsLoad / kLWaves; // x loads per wave per stage (4)
+constexpr int kLLoadsB = kLN / kLRowsLoad / kLWaves; // w loads per wave per stage (5)
+constexpr int kLEQ = 40;                       // columns per epilogue thread
+constexpr int kLERows = kLThreads / (kLN / kLEQ); // rows per epilogue round (64)
+constexpr int kLEStride = 352;                 // floats per epilogue row: 8 blocks of 40 columns, 44 apart
+// epilogue LDS index of (row, column): the 40-column blocks sit 44 floats apart and
+// every 4 rows 16 floats further on, so the threads' b128 reads (8 per row, 2 rows
+// per 16 lanes) and the accumulator stores (16 columns x 4 rows 4 apart) spread
+// over the banks
+__device__ __forceinline__ int lm_eidx(int r, int c) { return r * kLEStride + (r >> 2) * 16 + 44 * (c / kLEQ) + c % kLEQ; }
+static_assert(kLM == 2 * kLWM && kLN == 4 * kLWN && kLWaves == 8, "the wave layout the tile assumes");
+static_assert(kLLoadsA * kLRowsLoad * kLWaves == kLM && kLLoadsB * kLRowsLoad * kLWaves == kLN, "whole loads per wave");
+static_assert((kLERows * kLEStride + kLERows / 4 * 16) * 4 <= kLSmem, "an epilogue round fits the ring");
+static_assert(kLEQ % kLmMaxK == 0 && kLN % kLmMaxK == 0, "tiles and thread columns start at multiples of ngroups");
+static_assert(kLWM / 16 % 2 == 0 && kLERows == 2 * 16 * (kLM / kLWM), "a round is two block-rows of every wave row");
+
+// Chunk slot permutation of row r (its residue mod 16 decides): 8 consecutive
+// rows at one chunk cover 128 distinct bytes of the bank space, 16 rows 256.
+__device__ __forceinline__ int lm_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-// The 8 best keys seen, descending (0 = empty): insertion by compare-exchange.
-__device__ __forceinline__ void top8_insert(uint64_t (&t)[8], uint64_t key)
+// The N best keys seen, descending (0 = empty): insertion by compare-exchange.
+template <int N> __device__ __forceinline__ void topn_insert(uint64_t (&t)[N], uint64_t key)
 {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < N; ++i) {
         const uint64_t hi = key > t[i] ? key : t[i];
         key = key > t[i] ? t[i] : key;
         t[i] = hi;
     }
+}
+
+// Reductions over the 8 aligned lanes of this lane's octet: lane i meets 7 - i
+// (row_half_mirror), then its quad partners (quad_perm 1,0,3,2 and 2,3,0,1).
+__device__ __forceinline__ float octet_max(float v)
+{
+    v = fmaxf(v, dpp_f<0x141>(v));
+    v = fmaxf(v, dpp_f<0xb1>(v));
+    return fmaxf(v, dpp_f<0x4e>(v));
+}
+__device__ __forceinline__ float octet_sum(float v)
+{
+    v = v + dpp_f<0x141>(v);
+    v = v + dpp_f<0xb1>(v);
+    return v + dpp_f<0x4e>(v);
+}
+template <int CTRL> __device__ __forceinline__ uint64_t dpp_u64(uint64_t v)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xf, 0xf, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xf, 0xf, false);
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t octet_max_u64(uint64_t v)
+{
+    uint64_t o = dpp_u64<0x141>(v);
+    v = o > v ? o : v;
+    o = dpp_u64<0xb1>(v);
+    v = o > v ? o : v;
+    o = dpp_u64<0x4e>(v);
+    return o > v ? o : v;
+}
+
+// Wait until at most N of this wave's vector memory loads are in flight, then
+// meet the other waves. A direct-to-LDS load counts as done once its data is
+// in LDS, so after this every wave's loads issued before its last N are
+// visible. (A plain __syncthreads would wait for every load in flight.)
+template <int N> __device__ __forceinline__ void ring_barrier()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt field");
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0f70 | (N & 15) | ((N >> 4) << 14)); // vmcnt(N), expcnt and lgkmcnt at their maxima
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 template <int NG>
@@ -2071,9 +2152,9 @@ __global__ __launch_bounds__(kLThreads) void lmhead_tiles(const LmArgs a)
     __shared__ __align__(16) uint8_t smem[kLSmem];
     const int tid = threadIdx.x, lane = tid & (kLanes - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kLanes);
-    const int wm = wave >> 1, wn = wave & 1;
-    // tiles sharing a vocabulary slice are consecutive logical workgroups,
-    // hence on one XCD at about the same time: its weights come from HBM once
+    const int wm = wave >> 2, wn = wave & 3;
+    // the two row tiles of one vocabulary slice are consecutive logical
+    // workgroups, hence on one XCD at about the same time: w comes from HBM once
     const int L = logical_group((int)blockIdx.x, (int)gridDim.x);
     const int nt = L / a.mtiles, mt = L - nt * a.mtiles;
     const int m0 = mt * kLM, n0 = nt * kLN;
@@ -2082,208 +2163,308 @@ __global__ __launch_bounds__(kLThreads) void lmhead_tiles(const LmArgs a)
         const_cast<uint16_t *>(a.x), 0, (uint32_t)(a.M * a.H * 2), 0x00020000);
     const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(a.w), 0, (uint32_t)(a.V * a.H * 2), 0x00020000);
-    // this thread's 4 + 4 16-byte vectors of a stage: row (tid + 256 i) / 8, vector (tid + 256 i) mod 8
-    uint32_t goff_x[4], goff_w[4], loff[4];
+    // wave w loads x rows 8 (w + 8 q) + lane / 8 (q < 4) and w rows 8 (w + 8 q) + lane / 8
+    // (q < 5); lane mod 8 is the slot, holding chunk slot ^ swz(row)
+    const int lr = lane >> 3, lslot = lane & 7;
+    uint32_t gx[kLLoadsA], gw[kLLoadsB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int v = tid + kLThreads * i, r = v >> 3, kv = v & 7;
-        goff_x[i] = (uint32_t)(((m0 + r) * a.H + kv * 8) * 2);
-        goff_w[i] = (uint32_t)(((n0 + r) * a.H + kv * 8) * 2);
-        loff[i] = (uint32_t)((r * kLStride + kv * 8) * 2);
+    for (int q = 0; q < kLLoadsA; ++q) {
+        const int r = (wave + q * kLWaves) * kLRowsLoad + lr;
+        gx[q] = (uint32_t)(((m0 + r) * a.H + (lslot ^ lm_swz(r)) * 8) * 2);
     }
-    u32x4 gx[4], gw[4];
-    auto load_stage = [&](int k0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            gx[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, goff_x[i] + k0 * 2, 0, 0);
-            gw[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, goff_w[i] + k0 * 2, 0, kBufNT);
-        }
+    for (int q = 0; q < kLLoadsB; ++q) {
+        const int r = (wave + q * kLWaves) * kLRowsLoad + lr;
+        gw[q] = (uint32_t)(((n0 + r) * a.H + (lslot ^ lm_swz(r)) * 8) * 2);
+    }
+    auto issue = [&](int buf, int kt) {
+        uint8_t *st = smem + buf * kLStage;
+        const int soff = kt * kLRow;
+#pragma unroll
+        for (int q = 0; q < kLLoadsA; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rx, (lds_void *)(st + (wave + q * kLWaves) * kLRowsLoad * kLRow), 16, gx[q], soff, 0, 0);
+#pragma unroll
+        for (int q = 0; q < kLLoadsB; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rw, (lds_void *)(st + kLStageA + (wave + q * kLWaves) * kLRowsLoad * kLRow), 16, gw[q], soff, 0, 0);
     };
-    auto store_stage = [&](int st) {
-        uint8_t *A = smem + st * 2 * kLStage, *Bt = A + kLStage;
+    f32x4v acc[kLBI][kLBJ];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            *reinterpret_cast<u32x4 *>(A + loff[i]) = gx[i];
-            *reinterpret_cast<u32x4 *>(Bt + loff[i]) = gw[i];
-        }
-    };
-    f32x16 acc[2][2];
+    for (int i = 0; i < kLBI; ++i)
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                acc[i][j][e] = 0.f;
+        for (int j = 0; j < kLBJ; ++j)
+            acc[i][j] = f32x4v{0.f, 0.f, 0.f, 0.f};
     const int KT = a.H / kLK;
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
-    // operand rows of this lane: A row (or B column) lane mod 32 of each 32-block,
-    // k values 8 (lane / 32) .. + 7 of each 16-wide step (the same for A and B)
-    const int orow = lane & 31, okoff = (lane >> 5) * 8;
+    issue(0, 0);
+    // operands of this lane: A row (B column) lane mod 16 of each 16-block, k values
+    // 32 ks + 8 (lane / 16) .. + 7 of step ks, i.e. chunk 4 ks + lane / 16, at slot
+    // chunk ^ swz(row) (rows 16-aligned plus lane mod 16)
+    const int swz = lm_swz(lane & 15);
+    const int arow = (wm * kLWM + (lane & 15)) * kLRow, brow = kLStageA + (wn * kLWN + (lane & 15)) * kLRow;
+    int slot[kLK / 32];
+#pragma unroll
+    for (int ks = 0; ks < kLK / 32; ++ks)
+        slot[ks] = ((4 * ks + (lane >> 4)) ^ swz) * 16;
     for (int kt = 0; kt < KT; ++kt) {
-        const int st = kt & 1;
+        // stage kt is in LDS; after the barrier every wave is also done with the
+        // other buffer, which the next stage refills while this one is multiplied
+        ring_barrier<0>();
         if (kt + 1 < KT)
-            load_stage((kt + 1) * kLK);
-        const uint8_t *A = smem + st * 2 * kLStage, *Bt = A + kLStage;
+            issue((kt + 1) & 1, kt + 1);
+        const uint8_t *st = smem + (kt & 1) * kLStage;
 #pragma unroll
-        for (int ks = 0; ks < kLK / 16; ++ks) {
-            bf16x8 af[2], bf[2];
+        for (int ks = 0; ks < kLK / 32; ++ks) {
+            bf16x8 af[kLBI], bf[kLBJ];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                af[i] = *reinterpret_cast<const bf16x8 *>(
-                    A + ((wm * 64 + i * 32 + orow) * kLStride + ks * 16 + okoff) * 2);
-                bf[i] = *reinterpret_cast<const bf16x8 *>(
-                    Bt + ((wn * 64 + i * 32 + orow) * kLStride + ks * 16 + okoff) * 2);
-            }
+            for (int i = 0; i < kLBI; ++i)
+                af[i] = *reinterpret_cast<const bf16x8 *>(st + arow + i * 16 * kLRow + slot[ks]);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int j = 0; j < kLBJ; ++j)
+                bf[j] = *reinterpret_cast<const bf16x8 *>(st + brow + j * 16 * kLRow + slot[ks]);
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+            for (int i = 0; i < kLBI; ++i)
+#pragma unroll
+                for (int j = 0; j < kLBJ; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
         }
-        if (kt + 1 < KT)
-            store_stage(st ^ 1);
-        __syncthreads();
     }
 
-    // ---- the tile to LDS as [row][half][68 floats]: accumulator e of lane l in
-    // block (i, j) is row 32 i + 8 (e / 4) + 4 (l / 32) + e mod 4, column 32 j + l mod 32
+    // ---- epilogue, in 4 rounds: round rd takes block-rows 2 rd and 2 rd + 1 of
+    // every wave, 64 rows in LDS at lm_eidx; accumulator e of lane l in block
+    // (i, j) is row 16 i + 4 (l / 16) + e, column 16 j + l mod 16 of the wave's block
     float *E = reinterpret_cast<float *>(smem);
+    const int r = tid >> 3, o = tid & 7;           // this thread: epilogue row r, columns 40 o .. + 39
+    const int cbase = n0 + o * kLEQ;               // vocabulary index of its first column
+    const int nvalid = a.V - cbase;                // its columns inside the vocabulary (may be <= 0)
+    const float *er = E + lm_eidx(r, o * kLEQ);   // its 40 columns, contiguous
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int rd = 0; rd < kLBI / 2; ++rd) {
+        lds_barrier(); // the ring (first round) or the previous round's rows are done with
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int i2 = 0; i2 < 2; ++i2)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int r = wm * 64 + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
-                const int c = wn * 64 + j * 32 + (lane & 31);
-                E[(r * 2 + (c >> 6)) * kLHalf + (c & 63)] = acc[i][j][e];
+            for (int j = 0; j < kLBJ; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int row = wm * 32 + i2 * 16 + (lane >> 4) * 4 + e;
+                    const int c = wn * kLWN + j * 16 + (lane & 15);
+                    E[lm_eidx(row, c)] = acc[2 * rd + i2][j][e];
+                }
+        lds_barrier();
+        const int gm = m0 + (r >> 5) * kLWM + rd * 32 + (r & 31); // the row of logits (b * beam + j)
+        // this thread's 40 logits; columns past the vocabulary read as -inf
+        float v[kLEQ];
+#pragma unroll
+        for (int q = 0; q < kLEQ / 4; ++q) {
+            const float4 f = *reinterpret_cast<const float4 *>(er + 4 * q);
+            v[4 * q] = f.x;
+            v[4 * q + 1] = f.y;
+            v[4 * q + 2] = f.z;
+            v[4 * q + 3] = f.w;
+        }
+        if (nvalid < kLEQ) {
+#pragma unroll
+            for (int c = 0; c < kLEQ; ++c)
+                v[c] = c < nvalid ? v[c] : -INFINITY;
+        }
+        // pass A: group maxima (group = column mod NG; 40 o and n0 are multiples of NG),
+        // over the row's 8 threads
+        float gmx[NG];
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+            gmx[g] = v[g];
+#pragma unroll
+        for (int c = NG; c < kLEQ; ++c)
+            gmx[c % NG] = fmaxf(gmx[c % NG], v[c]);
+        float rmax = -INFINITY;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            gmx[g] = octet_max(gmx[g]);
+            rmax = fmaxf(rmax, gmx[g]);
+        }
+        // the threshold: the k-th largest of the NG group maxima (the least when k == NG)
+        float srt[NG];
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+            srt[g] = gmx[g];
+#pragma unroll
+        for (int x = 0; x < NG; ++x) // descending by exchanges (NG <= 8)
+#pragma unroll
+            for (int y = NG - 1; y > x; --y) {
+                const float hi = fmaxf(srt[y - 1], srt[y]), lo = fminf(srt[y - 1], srt[y]);
+                srt[y - 1] = hi;
+                srt[y] = lo;
             }
-    __syncthreads();
-
-    // ---- epilogue: thread (row r, half h) holds columns 64 h .. 64 h + 63 of row r
-    const int r = tid >> 1, h = tid & 1;
-    const int gm = m0 + r;          // the row of logits (b * beam + j)
-    const int cbase = n0 + h * 64;  // vocabulary index of this thread's first column
-    const int nvalid = a.V - cbase; // columns of this thread inside the vocabulary (may be <= 0)
-    const float *er = E + (r * 2 + h) * kLHalf;
-    // pass A: group maxima (group = column mod NG; 64 h is a multiple of NG)
-    float gmx[NG];
+        float T = srt[0];
 #pragma unroll
-    for (int g = 0; g < NG; ++g)
-        gmx[g] = -INFINITY;
+        for (int g = 1; g < NG; ++g)
+            T = g == a.k - 1 ? srt[g] : T;
+        // pass B: the log-sum-exp partial in base 2 around the row maximum, and the
+        // candidates (a -inf threshold, fewer than k groups in the vocabulary, takes
+        // every column inside it)
+        const float pm = rmax * kLog2e;
+        const float base = rmax == -INFINITY ? 0.f : pm;
+        float ssum = 0.f;
+        uint64_t cm = 0; // bit c: column c is a candidate
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-        const float4 v = *reinterpret_cast<const float4 *>(er + 4 * q);
-        const float vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int c = 4 * q + e;
-            gmx[c % NG] = c < nvalid ? fmaxf(gmx[c % NG], vv[e]) : gmx[c % NG];
+        for (int c = 0; c < kLEQ; ++c) {
+            ssum += fast_exp2(fmaf(v[c], kLog2e, -base));
+            cm |= (uint64_t)(v[c] >= T) << c;
         }
-    }
-    float rmax = -INFINITY;
+        cm &= nvalid >= kLEQ ? ~0ull : nvalid <= 0 ? 0ull : (1ull << nvalid) - 1ull;
+        ssum = octet_sum(ssum); // every lane of the octet holds a sum; the first one's is published
+        // this thread's NG best candidates by (logit desc, flat asc), then the row's
+        // k best by k rounds of an octet maximum
+        const int beamj = gm - (int)mdiv((uint32_t)gm, a.mb) * a.beam;
+        const uint32_t flat0 = (uint32_t)beamj * (uint32_t)a.V + (uint32_t)cbase;
+        uint64_t t[NG];
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-        gmx[g] = fmaxf(gmx[g], dpp_f<0xb1>(gmx[g])); // the partner half of the row (lane ^ 1)
-        rmax = fmaxf(rmax, gmx[g]);
-    }
-    // the threshold: the k-th largest of the NG group maxima (the least when k == NG)
-    float srt[NG];
-#pragma unroll
-    for (int g = 0; g < NG; ++g)
-        srt[g] = gmx[g];
-#pragma unroll
-    for (int i = 0; i < NG; ++i) // descending by exchanges (NG <= 8)
-#pragma unroll
-        for (int j = NG - 1; j > i; --j) {
-            const float hi = fmaxf(srt[j - 1], srt[j]), lo = fminf(srt[j - 1], srt[j]);
-            srt[j - 1] = hi;
-            srt[j] = lo;
+        for (int x = 0; x < NG; ++x)
+            t[x] = 0ull;
+        while (cm != 0) {
+            const int c = __builtin_ctzll(cm);
+            cm &= cm - 1;
+            topn_insert<NG>(t, score_key(er[c], flat0 + (uint32_t)c));
         }
-    float T = srt[0];
-#pragma unroll
-    for (int g = 1; g < NG; ++g)
-        T = g == a.k - 1 ? srt[g] : T;
-    // pass B: the log-sum-exp partial in base 2 around the row maximum, and the candidates
-    const float pm = rmax * kLog2e;
-    const float base = rmax == -INFINITY ? 0.f : pm;
-    float ssum = 0.f;
-    uint64_t cm = 0; // bit c: column c is a candidate (>= T, inside the vocabulary)
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-        const float4 v = *reinterpret_cast<const float4 *>(er + 4 * q);
-        const float vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int c = 4 * q + e;
-            const bool in = c < nvalid;
-            ssum += in ? fast_exp2(fmaf(vv[e], kLog2e, -base)) : 0.f;
-            cm |= (uint64_t)(in && vv[e] >= T) << c;
-        }
-    }
-    ssum = ssum + dpp_f<0xb1>(ssum);
-    // this half's 8 best candidates by (logit desc, flat asc)
-    const int beamj = gm - (int)mdiv((uint32_t)gm, a.mb) * a.beam;
-    const uint32_t flat0 = (uint32_t)beamj * (uint32_t)a.V + (uint32_t)cbase;
-    uint64_t t8[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        t8[i] = 0ull;
-    uint32_t nc = 0;
-    while (cm != 0) {
-        const int c = __builtin_ctzll(cm);
-        cm &= cm - 1;
-        top8_insert(t8, score_key(er[c], flat0 + (uint32_t)c));
-        ++nc;
-    }
-    __syncthreads(); // every thread is done with the tile before the lists replace it
-    // the two halves' lists side by side in LDS, each key ranked against all 16
-    uint64_t *lst = reinterpret_cast<uint64_t *>(smem) + r * 16;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        lst[h * 8 + i] = t8[i];
-    wave_sync(); // both halves of a row are in one wave
-    const uint32_t ntot = nc + (uint32_t)__builtin_amdgcn_update_dpp(0, (int)nc, 0xb1, 0xf, 0xf, false);
-    const uint32_t emit = ntot < (uint32_t)a.k ? ntot : (uint32_t)a.k;
-    if (gm < a.M) { // a row of the tile inside the batch
         const long long u = (long long)gm * a.C + nt; // the piece (row, tile)
+        uint64_t *sl = a.slots + u * a.k;
+        const bool own = gm < a.M && o == 0;          // a row inside the batch, written by its first thread
+        for (int x = 0; x < a.k; ++x) {
+            const uint64_t best = octet_max_u64(t[0]);
+            if (best != 0ull && t[0] == best) { // keys are unique: one thread of the octet owns it
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint64_t key = t8[i];
-            if (key == 0ull)
-                continue;
-            uint32_t rank = 0;
-#pragma unroll
-            for (int q = 0; q < 16; ++q)
-                rank += lst[q] > key;
-            if (rank < (uint32_t)a.k)
-                a.slots[u * a.k + rank] = key;
+                for (int y = 0; y + 1 < NG; ++y)
+                    t[y] = t[y + 1];
+                t[NG - 1] = 0ull;
+            }
+            if (own)
+                sl[x] = best; // 0: fewer candidates than k, the rest is empty
         }
-        if (h == 0) {
-            a.head[2 * u] = ((uint64_t)__float_as_uint(ssum) << 32) | __float_as_uint(pm);
-            a.head[2 * u + 1] = ((uint64_t)emit << 32) | __float_as_uint(T);
-        }
+        if (own)
+            a.ms[u] = ((uint64_t)__float_as_uint(ssum) << 32) | __float_as_uint(pm);
     }
 }
 
-// One workgroup per batch element: the per-piece path's selection over the
-// pieces lmhead_tiles published (heads, slots), into the outputs.
-__global__ __launch_bounds__(kLanes *kMaxWaves) void lmhead_merge(const StepArgs a)
+// lmhead_select: one workgroup per batch element, one wave per beam row.
+// A row's log-sum-exp merges its C partials (each lane its pieces in order,
+// then DPP reductions in a fixed order), its k best logits come from the union of its
+// pieces' top-k lists (exact by the chunk lemma), and each becomes the score
+// alive + (logit - lse) in fp32. A finished row offers (eos_id, alive) alone.
+// Wave 0 then takes the k best of the beam * k scores, ties to the lower flat
+// index, and pads with (-1, -1, -inf).
+constexpr int kLSelWaves = 16;
+constexpr int kLSelBatch = 4; // partials per lane per batch of loads (slot keys: 4x that)
+template <int NG>
+__global__ __launch_bounds__(kLanes *kLSelWaves) void lmhead_select(const LmArgs a)
 {
-    extern __shared__ __align__(16) uint8_t lds[];
-    GroupLds &g = *reinterpret_cast<GroupLds *>(lds);
+    __shared__ uint64_t cand[kLmMaxBeam * kLmMaxK];
     const int tid = threadIdx.x, lane = tid & (kLanes - 1);
-    const int W = (int)blockDim.x / kLanes;
-    const SortLds sm = sort_lds(lds + lds_header(W), a);
-    const int P = a.beam * a.chunks;
-    if (P <= kLanes && P * a.k <= 4 * kLanes) {
-        if (tid < kLanes)
-            sort_batch_wave(a, sm, (int)blockIdx.x, lane);
-    } else {
-        sort_batch(a, sm, g, (int)blockIdx.x, tid, W);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kLanes), W = (int)blockDim.x / kLanes;
+    const int b = (int)blockIdx.x;
+    for (int j = wave; j < a.beam; j += W) {
+        const long long row = (long long)b * a.beam + j;
+        uint64_t *cj = cand + j * a.k;
+        // the first batch of partials and keys, the running score and the finished
+        // flag all load at once (a finished row's pieces are read and ignored)
+        const uint64_t *ms = a.ms + row * a.C;
+        const uint64_t *sl = a.slots + row * a.C * a.k;
+        const int nkeys = a.C * a.k;
+        uint64_t vm[kLSelBatch], vk[4 * kLSelBatch];
+#pragma unroll
+        for (int q = 0; q < kLSelBatch; ++q) {
+            const int p = q * kLanes + lane;
+            vm[q] = p < a.C ? ms[p] : 0ull;
+        }
+#pragma unroll
+        for (int q = 0; q < 4 * kLSelBatch; ++q) {
+            const int i = q * kLanes + lane;
+            vk[q] = i < nkeys ? sl[i] : 0ull;
+        }
+        const float alive = a.alive[row];
+        if (a.finished != nullptr && a.finished[row] != 0) {
+            if (lane < a.k)
+                cj[lane] = lane == 0 ? score_key(alive, (uint32_t)j * (uint32_t)a.V + (uint32_t)a.eos_id) : 0ull;
+            continue;
+        }
+        float m = -INFINITY, s = 0.f;
+        uint64_t t[NG];
+#pragma unroll
+        for (int i = 0; i < NG; ++i)
+            t[i] = 0ull;
+        for (int p0 = 0;;) { // each lane its partials in order of p
+#pragma unroll
+            for (int q = 0; q < kLSelBatch; ++q)
+                if (p0 + q * kLanes + lane < a.C)
+                    lse_merge(m, s, __uint_as_float((uint32_t)vm[q]), __uint_as_float((uint32_t)(vm[q] >> 32)));
+            p0 += kLSelBatch * kLanes;
+            if (p0 >= a.C)
+                break;
+#pragma unroll
+            for (int q = 0; q < kLSelBatch; ++q) {
+                const int p = p0 + q * kLanes + lane;
+                vm[q] = p < a.C ? ms[p] : 0ull;
+            }
+        }
+        for (int q0 = 0;;) {
+#pragma unroll
+            for (int q = 0; q < 4 * kLSelBatch; ++q)
+                topn_insert<NG>(t, vk[q]);
+            q0 += 4 * kLSelBatch * kLanes;
+            if (q0 >= nkeys)
+                break;
+#pragma unroll
+            for (int q = 0; q < 4 * kLSelBatch; ++q) {
+                const int i = q0 + q * kLanes + lane;
+                vk[q] = i < nkeys ? sl[i] : 0ull;
+            }
+        }
+        // the wave's maximum, then the sum of the lanes' sums rescaled to it (DPP, fixed order)
+        const float M = wave_max_f(m);
+        const float S = wave_sum_f(m == -INFINITY ? 0.f : s * fast_exp2(m - M));
+        const float lse = (M + fast_log2(S)) * kLn2;
+        for (int i = 0; i < a.k; ++i) {
+            const uint64_t best = wave_max_key(t[0]);
+            if (best != 0ull && t[0] == best) { // keys are unique: one lane owns it
+#pragma unroll
+                for (int q = 0; q + 1 < NG; ++q)
+                    t[q] = t[q + 1];
+                t[NG - 1] = 0ull;
+            }
+            if (lane == 0)
+                cj[i] = best == 0ull ? 0ull : score_key(alive + (entry_x(best) - lse), entry_flat(best));
+        }
+    }
+    __syncthreads();
+    if (wave != 0)
+        return;
+    uint64_t t[NG];
+#pragma unroll
+    for (int i = 0; i < NG; ++i)
+        t[i] = 0ull;
+    for (int q = lane; q < a.beam * a.k; q += kLanes)
+        topn_insert<NG>(t, cand[q]);
+    for (int p = 0; p < a.k; ++p) {
+        const uint64_t best = wave_max_key(t[0]);
+        if (best != 0ull && t[0] == best) {
+#pragma unroll
+            for (int q = 0; q + 1 < NG; ++q)
+                t[q] = t[q + 1];
+            t[NG - 1] = 0ull;
+        }
+        if (lane == 0) {
+            const long long o = (long long)b * a.k + p;
+            if (best != 0ull) {
+                const uint32_t flat = entry_flat(best), jj = mdiv(flat, a.mv);
+                a.out_beam[o] = (int32_t)jj;
+                a.out_token[o] = (int32_t)(flat - jj * (uint32_t)a.V);
+                a.out_score[o] = entry_x(best);
+            } else { // fewer than k candidates at all
+                a.out_beam[o] = -1;
+                a.out_token[o] = -1;
+                a.out_score[o] = -INFINITY;
+            }
+        }
     }
 }
 #endif
@@ -2338,24 +2519,28 @@ hipError_t launch_zero(void *p, size_t bytes, hipStream_t stream)
 #endif
 
 #if RTOPK_DTYPE == 2
-hipError_t launch_lmhead(const LmArgs &la, const StepArgs &a, size_t merge_lds, hipStream_t s)
+hipError_t launch_lmhead(const LmArgs &a, hipStream_t s)
 {
-    const dim3 grid((unsigned)(la.mtiles * la.C)), block(kLThreads);
-    switch (la.ngroups) {
-    case 1: hipLaunchKernelGGL(lmhead_tiles<1>, grid, block, 0, s, la); break;
-    case 2: hipLaunchKernelGGL(lmhead_tiles<2>, grid, block, 0, s, la); break;
-    case 4: hipLaunchKernelGGL(lmhead_tiles<4>, grid, block, 0, s, la); break;
-    case 8: hipLaunchKernelGGL(lmhead_tiles<8>, grid, block, 0, s, la); break;
+    const dim3 grid((unsigned)(a.mtiles * a.C)), block(kLThreads);
+    const dim3 sgrid((unsigned)a.B), sblock(kLanes * (a.beam < kLSelWaves ? a.beam : kLSelWaves));
+    switch (a.ngroups) {
+    case 1: hipLaunchKernelGGL(lmhead_tiles<1>, grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL(lmhead_tiles<2>, grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL(lmhead_tiles<4>, grid, block, 0, s, a); break;
+    case 8: hipLaunchKernelGGL(lmhead_tiles<8>, grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(lmhead_merge, dim3((unsigned)a.B), dim3(kLanes * a.waves), merge_lds, s, a);
+    switch (a.ngroups) {
+    case 1: hipLaunchKernelGGL(lmhead_select<1>, sgrid, sblock, 0, s, a); break;
+    case 2: hipLaunchKernelGGL(lmhead_select<2>, sgrid, sblock, 0, s, a); break;
+    case 4: hipLaunchKernelGGL(lmhead_select<4>, sgrid, sblock, 0, s, a); break;
+    default: hipLaunchKernelGGL(lmhead_select<8>, sgrid, sblock, 0, s, a); break;
+    }
     return hipGetLastError();
 }
-
-size_t lmhead_merge_lds(int waves, size_t sort_bytes) { return lds_header(waves) + sort_bytes; }
 #endif
 
 template <>

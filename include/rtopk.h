@@ -296,20 +296,22 @@ int rtopk_sample_step(const void *logits, int dtype, int R, int V, int k, float 
  * fuses the work around its GEMMs into them (kernel-fusion passage). Here
  *     logits[b*beam + j][t] = sum_h hidden[b*beam + j][h] * weight[t][h]
  * (bfloat16 inputs, float32 accumulation on the matrix cores) are computed
- * in 128 x 128 tiles whose epilogue runs pass 1 and the per-piece top-k of
- * the selection (a piece = one row of one 128-wide vocabulary tile; its
- * groups are the vocabulary indices mod ngroups), so the [B*beam][V] logits
- * never reach HBM; a second launch then selects each batch element exactly
- * as rtopk_beam_step does. Results are those of rtopk_beam_step on the
- * float32 logits of that GEMM.
+ * in 256-row x 320-column tiles whose epilogue runs pass 1 and the per-piece
+ * top-k of the selection (a piece = one row of one 320-wide vocabulary tile;
+ * its groups are the vocabulary indices mod ngroups), so the [B*beam][V]
+ * logits never reach HBM; a second launch merges each row's pieces (its
+ * log-sum-exp and its k best logits) and selects each batch element with the
+ * scores, order, finished-beam rule and padding of rtopk_beam_step. Results
+ * are those of rtopk_beam_step on the float32 logits of that GEMM.
  *   hidden   device [B*beam][H] bfloat16 (row b*beam + j is beam j of batch element b)
  *   weight   device [V][H] bfloat16, one row per vocabulary entry (the output
  *            projection as a [V][H] matrix); both 16-byte aligned
  *   H        a multiple of 64 (else RTOPK_ENOTSUP)
  *   k        1 <= k <= min(8, beam*V) (k > 8: RTOPK_ENOTSUP)
- * Everything else as rtopk_beam_step (library-owned workspace of `stream`).
- * RTOPK_ENOTSUP also when beam * ceil(V / 128) > 3072 or hidden or weight
- * spans 2 GiB or more.
+ * Everything else as rtopk_beam_step (library-owned workspace of `stream`,
+ * 8 * B*beam * ceil(V/320) * (k + 1) bytes past its fixed region).
+ * RTOPK_ENOTSUP also when beam > 512 or hidden or weight spans about 2 GiB
+ * or more (32-bit buffer offsets, counted to the end of the last tile).
  */
 int rtopk_lmhead_step(const void *hidden, const void *weight, const float *alive_scores,
                       const uint8_t *finished_mask, int B, int beam, int H, int V, int k, int eos_id,

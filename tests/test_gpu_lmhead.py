@@ -62,12 +62,14 @@ def _check(x, w, alive, fin, beam, k, eos, got, rows_of=None):
 
 
 @pytest.mark.parametrize("B,beam,H,V,k,nfin", [
-    (2, 2, 64, 300, 2, 0),       # two vocabulary tiles, the second ragged
-    (3, 4, 128, 1000, 4, 2),     # 12 rows (one ragged row tile), finished beams
-    (5, 1, 64, 7, 1, 0),         # V < 128, k = 1
+    (2, 2, 64, 300, 2, 0),       # one 320-wide vocabulary tile, ragged inside a thread's 40 columns
+    (2, 2, 64, 700, 2, 0),       # three vocabulary tiles, the last 60 wide (whole threads past V)
+    (3, 4, 128, 1000, 4, 2),     # 12 rows of one 256-row tile, finished beams
+    (5, 1, 64, 7, 1, 0),         # V < 40: part of one thread's columns, k = 1
     (2, 8, 192, 2000, 8, 3),     # k = 8 (8 groups), beam = 8
-    (4, 4, 64, 640, 5, 1),       # k = 5: the 5th largest of 8 group maxima
-    (33, 4, 256, 4100, 4, 6),    # 132 rows: two row tiles, the second with 4 rows
+    (4, 4, 64, 640, 5, 1),       # k = 5: the 5th largest of 8 group maxima; two whole tiles
+    (65, 4, 64, 700, 4, 5),      # 260 rows: two row tiles, the second with 4 rows
+    (33, 4, 256, 4100, 4, 6),    # 132 rows, 13 vocabulary tiles
     (1, 3, 64, 128, 3, 3),       # every beam finished
 ])
 def test_lmhead_matches_oracle(B, beam, H, V, k, nfin):
