@@ -794,6 +794,24 @@ int rtopk_read_probe(const void *src, size_t bytes, uint32_t marker, uint32_t *o
     return RTOPK_OK;
 }
 
+int rtopk_read_probe_shape(const void *src, size_t bytes, int vecs_per_lane, int threads, uint32_t marker,
+                           uint32_t *out, void *stream)
+{
+    if (src == nullptr || out == nullptr)
+        return fail(RTOPK_EINVAL, "read probe: NULL pointer");
+    if ((uintptr_t)src % 16 != 0 || bytes % 16 != 0)
+        return fail(RTOPK_EINVAL, "read probe: src must be 16-byte aligned and bytes a multiple of 16");
+    const int v = vecs_per_lane;
+    if (!(v == 1 || v == 2 || v == 4 || v == 8 || v == 10 || v == 16))
+        return fail(RTOPK_EINVAL, "read probe: vecs_per_lane=%d is not 1, 2, 4, 8, 10 or 16", v);
+    if (threads < 64 || threads > 1024 || threads % 64 != 0)
+        return fail(RTOPK_EINVAL, "read probe: threads=%d is not a multiple of 64 in [64, 1024]", threads);
+    const hipError_t e = rtopk::launch_read_probe_shape(src, bytes, v, threads, marker, out, (hipStream_t)stream);
+    if (e != hipSuccess)
+        return fail(RTOPK_EHIP, "read probe launch: %s", hipGetErrorString(e));
+    return RTOPK_OK;
+}
+
 const char *rtopk_last_error(void) { return g_err.c_str(); }
 
 void rtopk_release(void)

@@ -142,6 +142,8 @@ long long reorder_chunk_bytes();
 hipError_t launch_beam_reorder(const void *src, void *dst, long long nslabs, int B, int beam, long long row_bytes,
                                const int32_t *ids, int ld, hipStream_t stream);
 hipError_t launch_read_probe(const void *src, size_t bytes, uint32_t marker, uint32_t *out, hipStream_t stream);
+hipError_t launch_read_probe_shape(const void *src, size_t bytes, int vecs, int threads, uint32_t marker,
+                                   uint32_t *out, hipStream_t stream);
 
 // The status and thread-local message of the C ABI's last error (rtopk_last_error).
 int set_error(int status, const char *fmt, ...);

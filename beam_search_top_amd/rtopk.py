@@ -91,6 +91,8 @@ def load():
     L.rtopk_beam_reorder.restype = i32
     L.rtopk_read_probe.argtypes = [vp, sz, ctypes.c_uint32, vp, vp]
     L.rtopk_read_probe.restype = i32
+    L.rtopk_read_probe_shape.argtypes = [vp, sz, i32, i32, ctypes.c_uint32, vp, vp]
+    L.rtopk_read_probe_shape.restype = i32
     L.rtopk_last_error.argtypes = []
     L.rtopk_last_error.restype = ctypes.c_char_p
     L.rtopk_release.argtypes = []
@@ -265,6 +267,10 @@ def rtopk_beam_reorder(src, dst, nslabs, B, beam, row_bytes, beam_ids, ld, strea
 
 def rtopk_read_probe(src, nbytes, marker, out, stream):
     return load().rtopk_read_probe(src, nbytes, marker, out, stream)
+
+
+def rtopk_read_probe_shape(src, nbytes, vecs_per_lane, threads, marker, out, stream):
+    return load().rtopk_read_probe_shape(src, nbytes, vecs_per_lane, threads, marker, out, stream)
 
 
 def rtopk_last_error():

@@ -342,20 +342,103 @@ def bench_lmhead(args):
     print(json.dumps(line), flush=True)
 
 
+def usable_cpus():
+    """CPUs this process may run on: its affinity set, bounded by the cgroup's
+    CPU quota when one is set (a container's share of a larger host)."""
+    n = len(os.sched_getaffinity(0))
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            quota, period = f.read().split()[:2]
+        if quota != "max":
+            n = min(n, max(1, int(int(quota) // int(period))))
+    except (OSError, ValueError):
+        pass
+    return n
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(s, seconds):
+    """The oracle, untuned, on this host's cores: once single-threaded and once
+    with every usable CPU, each repeated until it has run seconds / 2 (at
+    least one step)."""
     import oracle
-    threads = max(1, min(16, len(os.sched_getaffinity(0))))
-    oracle.step_of(s, nthreads=threads)  # warm (page-in)
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.step_of(s, nthreads=threads)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or reps >= 1000:
-            break
-    return {"value": reps / el, "unit": "beam-steps/s", "cores": threads, "kind": "oracle",
-            "sample": f"{reps} full {s.name} steps (B={s.B} beam={s.beam} V={s.V}) in {el:.1f} s, "
-                      f"float64 log-softmax + full sort per batch element, {threads} threads"}
+    threads = usable_cpus()
+
+    def rate(nthreads):
+        oracle.step_of(s, nthreads=nthreads)  # warm (page-in)
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            oracle.step_of(s, nthreads=nthreads)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds / 2 or reps >= 1000:
+                return reps, el
+
+    r1, e1 = rate(1)
+    rt, et = rate(threads)
+    return {"value": rt / et, "unit": "beam-steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rt} full {s.name} steps (B={s.B} beam={s.beam} V={s.V}) in {et:.1f} s with {threads} "
+                      f"threads, {r1} in {e1:.1f} s with 1; float64 log-softmax + full sort per batch element",
+            "single_thread": {"value": r1 / e1, "unit": "beam-steps/s", "cores": 1},
+            "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model()}
+
+
+def read_sweep(L, cur):
+    """Plain streaming reads (rtopk_read_probe_shape) of 38.88 MB (the
+    algorithmic bytes of the b128 step) and of 256 MiB, for several launch
+    shapes, each over a pool of distinct buffers larger than the Infinity
+    Cache and replayed from a captured graph; prints one line per shape."""
+    import torch
+    pool_bytes = 1 << 30
+    for nbytes in (38_880_000, 256 << 20):
+        nbuf = max(2, -(-pool_bytes // nbytes))
+        bufs = [torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1) for _ in range(nbuf)]
+        out = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+        for vecs in (1, 2, 4, 8, 10, 16):
+            for threads in (256, 512, 1024):
+                def probe(i, stream):
+                    rc = L.rtopk_read_probe_shape(bufs[i % nbuf].data_ptr(), nbytes, vecs, threads, 0x7fc00001,
+                                                  out.data_ptr(), stream)
+                    if rc != 0:
+                        raise RuntimeError("read probe failed")
+                for i in range(10):
+                    probe(i, cur.cuda_stream)
+                graph = torch.cuda.CUDAGraph()
+                cs = torch.cuda.Stream()
+                cs.wait_stream(cur)
+                n_in = 20
+                with torch.cuda.graph(graph, stream=cs):
+                    for i in range(n_in):
+                        probe(i, torch.cuda.current_stream().cuda_stream)
+                torch.cuda.synchronize()
+                graph.replay()
+                torch.cuda.synchronize()
+                times = []
+                for _ in range(5):
+                    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    start.record(cur)
+                    for _ in range(5):
+                        graph.replay()
+                    end.record(cur)
+                    torch.cuda.synchronize()
+                    times.append(start.elapsed_time(end) * 1e3 / (5 * n_in))
+                us = sorted(times)[2]
+                grid = -(-nbytes // (16 * vecs * threads))
+                print(json.dumps({"bytes": nbytes, "vecs_per_lane": vecs, "threads": threads, "grid": grid,
+                                  "us_per_launch": round(us, 3), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                                  "frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}),
+                      flush=True)
+        del bufs
 
 
 def main():
@@ -378,6 +461,8 @@ def main():
     ap.add_argument("--no-read-ceiling", action="store_true", help="skip the plain-read ceiling measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 256 MiB device copy (reference kernel for HBM counters)")
+    ap.add_argument("--read-sweep", action="store_true",
+                    help="print plain-read times for several launch shapes at 38.88 MB and 256 MiB, then exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the selection step of a batch "
@@ -392,6 +477,12 @@ def main():
         return
     if args.path == "lmhead":
         bench_lmhead(args)
+        return
+    if args.read_sweep:
+        import torch
+
+        from beam_search_top_amd import rtopk
+        read_sweep(rtopk.load(), torch.cuda.current_stream())
         return
 
     import numpy as np
@@ -468,27 +559,31 @@ def main():
             graph.replay()
         torch.cuda.synchronize()
 
-    def timed(mode):
+    def timed(mode, n):
         start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         start.record(cur)
         if mode == "graph":
-            for _ in range(K // glen):
+            for _ in range(n // glen):
                 graph.replay()
-            for i in range(K % glen):
+            for i in range(n % glen):
                 launch(i, cur.cuda_stream)
         else:
-            for i in range(K):
+            for i in range(n):
                 launch(i, cur.cuda_stream)
         end.record(cur)
         torch.cuda.synchronize()
         return start.elapsed_time(end)
 
-    ms_total = timed(args.launch)
-    ms_step = ms_total / K
-    other = {}
+    # the GPU time: K steps in 5 trials (K / 5 steps each, the last takes the
+    # remainder), each bracketed by events and synchronisation; the median trial
+    ntr = min(5, K)
+    sizes = [K // ntr] * (ntr - 1) + [K - (K // ntr) * (ntr - 1)]
+    trials = [timed(args.launch, n) / n for n in sizes]
+    ms_step = float(np.median(trials))
+    other = {"trials_ms_per_step": [round(t, 6) for t in trials], "trial_steps": sizes}
     if args.launch == "graph":
-        other["eager_ms_per_step"] = round(timed("eager") / K, 6)
+        other["eager_ms_per_step"] = round(timed("eager", K) / K, 6)
 
     # the last step's outputs come from buffer (K-1) % nbuf; re-run buffer 0 for a sanity check
     launch(0, cur.cuda_stream)

@@ -34,9 +34,8 @@
  *    only when finished beams leave fewer than k), the tail is padded with
  *    beam = token = -1 and score = -inf.
  *  - A finished beam (finished_mask != 0) offers the single continuation
- *    (j, eos_id) at its unchanged running score; its logits are never used.
- *    (The kernel issues a piece's loads before the flag arrives, so a finished
- *    row is still read once: that costs less than waiting for the flag.)
+ *    (j, eos_id) at its unchanged running score; its logits are never read
+ *    (the flag sizes the row's loads to zero bytes).
  *  - Scores are computed in float32: alive + (logit - lse), lse accumulated in
  *    float32 in a fixed order, so results are bit-reproducible across calls.
  *  - NaN or +inf logits, and alive beams whose logits are all -inf, are
@@ -351,6 +350,15 @@ int rtopk_beam_reorder(const void *src, void *dst, long long nslabs, int B, int 
  * Asynchronous on `stream`; allocates nothing.
  */
 int rtopk_read_probe(const void *src, size_t bytes, uint32_t marker, uint32_t *out, void *stream);
+
+/*
+ * The same measurement aid with the launch shape chosen by the caller:
+ * vecs_per_lane 16-byte loads per lane (1, 2, 4, 8, 10 or 16) and `threads`
+ * lanes per workgroup (a multiple of 64 in [64, 1024]); else as
+ * rtopk_read_probe. RTOPK_EINVAL also for another vecs_per_lane or threads.
+ */
+int rtopk_read_probe_shape(const void *src, size_t bytes, int vecs_per_lane, int threads, uint32_t marker,
+                           uint32_t *out, void *stream);
 
 /* Thread-local description of the last non-OK status ("" if none). */
 const char *rtopk_last_error(void);

@@ -161,6 +161,10 @@ def test_read_probe_validation(lib):
     assert rtopk.rtopk_read_probe(0x1000, 72, 0, 0x2000, None) == rtopk.RTOPK_EINVAL
     assert rtopk.rtopk_read_probe(None, 64, 0, 0x2000, None) == rtopk.RTOPK_EINVAL
     assert rtopk.rtopk_read_probe(0x1000, 64, 0, None, None) == rtopk.RTOPK_EINVAL
+    assert rtopk.rtopk_read_probe_shape(0x1000, 64, 3, 256, 0, 0x2000, None) == rtopk.RTOPK_EINVAL
+    assert rtopk.rtopk_read_probe_shape(0x1000, 64, 4, 96, 0, 0x2000, None) == rtopk.RTOPK_EINVAL
+    assert rtopk.rtopk_read_probe_shape(0x1000, 64, 4, 2048, 0, 0x2000, None) == rtopk.RTOPK_EINVAL
+    assert rtopk.rtopk_read_probe_shape(0x1008, 64, 4, 256, 0, 0x2000, None) == rtopk.RTOPK_EINVAL
     assert "read probe" in rtopk.rtopk_last_error()
 
 
