@@ -2278,7 +2278,8 @@ __global__ __launch_bounds__(kLThreads) void lmhead_tiles(const LmArgs a)
                 }
         lds_barrier();
         const int gm = m0 + (r >> 5) * kLWM + rd * 32 + (r & 31); // the row of logits (b * beam + j)
-        // this thread's 40 logits; columns past the vocabulary read as -inf
+        // this thread's 40 logits; columns past the vocabulary read as -inf (a
+        // wave-uniform branch: only the waves of the last vocabulary tile take it)
         float v[kLEQ];
 #pragma unroll
         for (int q = 0; q < kLEQ / 4; ++q) {
@@ -2288,7 +2289,7 @@ __global__ __launch_bounds__(kLThreads) void lmhead_tiles(const LmArgs a)
             v[4 * q + 2] = f.z;
             v[4 * q + 3] = f.w;
         }
-        if (nvalid < kLEQ) {
+        if (ballot(nvalid < kLEQ) != 0) {
 #pragma unroll
             for (int c = 0; c < kLEQ; ++c)
                 v[c] = c < nvalid ? v[c] : -INFINITY;
