@@ -48,6 +48,7 @@ std::atomic<int> g_override_nv{0};
 std::atomic<int> g_override_limit{0};
 std::atomic<int> g_override_waves{0};
 std::atomic<int> g_rowlocal{1};
+std::atomic<int> g_split{1};
 std::atomic<unsigned> g_spin_limit{rtopk::kDefaultSpinLimit};
 
 const int kVecsPerThread[] = {1, 2, 3, 4, 6, 8, 10, 12};
@@ -202,6 +203,10 @@ int make_plan(const void *logits, int B, int beam, int V, int k, int dtype, rtop
     // row-local lists go through the mailbox of the workspace's fixed region
     if (p->rowlocal && (long long)B * p->maxl * k > rtopk::kMailboxSlots)
         p->rowlocal = 0;
+    // Per-piece publication in rounds (more pieces than the GPU holds at once):
+    // the per-batch selection becomes a second launch (measured on 64 x 8 x
+    // 250000 bf16, see rtopk_select)
+    p->split = !p->rowlocal && rows * C > kResidentPieces && g_split.load() ? 1 : 0;
     if (rows * C >= (1ll << 31)) // piece indices are 31-bit in the kernel
         return fail(RTOPK_ENOTSUP, "%lld pieces are too many", rows * C);
     if ((long long)beam * C > rtopk::kMaxPieces)
@@ -221,6 +226,7 @@ int make_plan(const void *logits, int B, int beam, int V, int k, int dtype, rtop
     const size_t pieces = (size_t)beam * (size_t)C;
     const size_t sort_lds = 8 * (size_t)p->sort_keys + 13 * pieces + 13 * (size_t)beam;
     p->lds_bytes = (rtopk::group_lds_bytes(p->waves, sort_lds, p->rowlocal != 0, k, p->maxl) + 15) & ~size_t(15);
+    p->select_lds = (rtopk::select_lds_bytes(sort_lds) + 15) & ~size_t(15);
 
     if (B > rtopk::kTicketCap)
         return fail(RTOPK_ENOTSUP, "B=%d exceeds the implementation limit %d", B, rtopk::kTicketCap);
@@ -298,6 +304,7 @@ int enqueue(const rtopk::Plan &p, const void *logits, int dtype, const float *al
     a.sort_keys = p.sort_keys;
     a.waves = p.waves;
     a.rowlocal = p.rowlocal;
+    a.split = p.split;
     a.maxl = p.maxl;
     a.mc = rtopk::make_magic((uint32_t)p.chunks);
     a.mb = rtopk::make_magic((uint32_t)beam);
@@ -327,6 +334,8 @@ int enqueue(const rtopk::Plan &p, const void *logits, int dtype, const float *al
     hipError_t e = dtype == RTOPK_F32   ? rtopk::launch_dtype<0>(a, p.vecs_per_thread, p.lds_bytes, stream)
                    : dtype == RTOPK_F16 ? rtopk::launch_dtype<1>(a, p.vecs_per_thread, p.lds_bytes, stream)
                                         : rtopk::launch_dtype<2>(a, p.vecs_per_thread, p.lds_bytes, stream);
+    if (e == hipSuccess && p.split)
+        e = rtopk::launch_select(a, p.select_lds, stream);
     if (e != hipSuccess)
         return fail(RTOPK_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
     return RTOPK_OK;
@@ -579,6 +588,12 @@ int rtopk_set_override(int vecs_per_thread, int chunk_limit)
 int rtopk_set_row_local(int enable)
 {
     g_rowlocal.store(enable != 0 ? 1 : 0);
+    return RTOPK_OK;
+}
+
+int rtopk_set_split(int enable)
+{
+    g_split.store(enable != 0 ? 1 : 0);
     return RTOPK_OK;
 }
 

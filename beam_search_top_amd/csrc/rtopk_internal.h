@@ -63,6 +63,7 @@ struct StepArgs {
     int sort_keys;                 // LDS sort keys of the per-batch selection (power of two)
     int waves;                     // pieces (waves) per workgroup, <= kMaxWaves
     int rowlocal;                  // workgroups hold whole rows (chunks divides waves)
+    int split;                     // per-piece path: pieces only publish; rtopk_select selects
     int maxl;                      // row-local: workgroup lists per batch element, at most
     unsigned spin_limit;           // row-local: polls of the mailbox before the merge gives up
     Magic mc, mb, mp, mw, mv;      // division by chunks, beam, beam*chunks, waves, V
@@ -99,6 +100,8 @@ struct Plan {
     int elem_bytes, epv;
     int chunks, vecs_per_thread, vecs_per_chunk;
     int ngroups, chunk_limit, queue_cap, align_elems, sort_keys, waves, rowlocal, maxl;
+    int split; // per-piece publication in rounds: the per-batch selection is a second launch
+    size_t select_lds; // LDS bytes of that launch
     int nshards, vshard, cps; // vocabulary shards, logits per shard row, pieces per shard row
     long long grid;
     size_t lds_bytes;
@@ -109,6 +112,9 @@ struct Plan {
 // 1 float16, 2 bfloat16). Returns a hipError_t.
 template <int DT>
 hipError_t launch_dtype(const StepArgs &a, int vecs_per_thread, size_t lds_bytes, hipStream_t stream);
+// Enqueue the per-batch selection of a split step (one workgroup of a.waves
+// waves per batch element over the pieces the step kernel published).
+hipError_t launch_select(const StepArgs &a, size_t lds_bytes, hipStream_t stream);
 
 // The LM head fused with pass 1 (rtopk_kernels.hip, bfloat16 unit).
 struct LmArgs {
@@ -156,6 +162,8 @@ bool supported_vecs_per_thread(int nv);
 // Dynamic LDS of a workgroup of `waves` pieces whose per-batch selection
 // needs sort_bytes (and, row-local, keys for the workgroup's own selection).
 size_t group_lds_bytes(int waves, size_t sort_bytes, bool rowlocal, int k, int maxl);
+// LDS of rtopk_select (kMaxWaves waves) for a selection of sort_bytes.
+size_t select_lds_bytes(size_t sort_bytes);
 
 // Row-local workgroups: LDS keys of the workgroup's own selection (every
 // candidate of its pieces plus one per finished row) followed, in the

@@ -1994,12 +1994,40 @@ __global__ __launch_bounds__(kLanes *kMaxWaves) void rtopk_step(const StepArgs a
                           (int)mdiv((uint32_t)rlast, a.mb), rfirst, rlast, lane);
     } else {
         piece_compute<DT, NV, MODE, false>(a, sm, P, u, lane);
+        if (a.split) // the selection is a second launch, once every piece has published
+            return;
         lds_barrier();
         rtopk_step_tail(a, g, lds, hdr, tid, lane, wave, W, ufirst, ulast);
     }
 }
 
 #if RTOPK_DTYPE == 0
+// The per-batch selection of a split step: when the step's workgroups run in
+// rounds, a workgroup that completed a batch element would hold its CU for the
+// selection while later workgroups wait to stream, and the last round's
+// selections would all come after the stream. Instead the step kernel only
+// publishes, and this launch selects every batch element at once (one
+// workgroup each) from the same published pieces, with the same code as the
+// in-kernel tail. The kernel boundary orders the pieces' stores before these
+// reads; no ticket is counted.
+// It runs kMaxWaves waves whatever the step's workgroup size, so that the
+// speculative loads of sort_batch cover every published slot at once.
+__global__ __launch_bounds__(kLanes *kMaxWaves) void rtopk_select(const StepArgs a)
+{
+    extern __shared__ __align__(16) uint8_t lds[];
+    GroupLds &g = *reinterpret_cast<GroupLds *>(lds);
+    const int tid = threadIdx.x, lane = tid & (kLanes - 1);
+    const int W = (int)blockDim.x / kLanes;
+    const SortLds sm = sort_lds(lds + lds_header(W), a);
+    const int P = a.beam * a.chunks;
+    if (P <= kLanes && P * a.k <= 4 * kLanes) {
+        if (tid < kLanes)
+            sort_batch_wave(a, sm, (int)blockIdx.x, lane);
+    } else {
+        sort_batch(a, sm, g, (int)blockIdx.x, tid, W);
+    }
+}
+
 // Plain streaming read (measurement aid): kReadVecs 16-byte vectors per lane,
 // consecutive lanes on consecutive vectors, all loads issued before any use.
 constexpr int kReadVecs = 10;
@@ -2499,6 +2527,8 @@ __global__ __launch_bounds__(kLanes *kLSelWaves) void lmhead_select(const LmArgs
 
 #if RTOPK_DTYPE == 0
 
+size_t select_lds_bytes(size_t sort_bytes) { return lds_header(kMaxWaves) + sort_bytes; }
+
 size_t group_lds_bytes(int waves, size_t sort_bytes, bool rowlocal, int k, int maxl)
 {
     const size_t sel = (size_t)waves * sizeof(SelectLds);
@@ -2515,6 +2545,12 @@ bool supported_vecs_per_thread(int nv)
     default:
         return false;
     }
+}
+
+hipError_t launch_select(const StepArgs &a, size_t lds_bytes, hipStream_t stream)
+{
+    hipLaunchKernelGGL(rtopk_select, dim3((unsigned)a.B), dim3(kLanes * kMaxWaves), lds_bytes, stream, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_read_probe(const void *src, size_t bytes, uint32_t marker, uint32_t *out, hipStream_t stream)

@@ -73,6 +73,8 @@ def load():
     L.rtopk_set_override.restype = i32
     L.rtopk_set_row_local.argtypes = [i32]
     L.rtopk_set_row_local.restype = i32
+    L.rtopk_set_split.argtypes = [i32]
+    L.rtopk_set_split.restype = i32
     L.rtopk_set_waves.argtypes = [i32]
     L.rtopk_set_waves.restype = i32
     L.rtopk_set_spin_limit.argtypes = [ctypes.c_uint]
@@ -152,6 +154,10 @@ def rtopk_set_override(vecs_per_thread, chunk_limit):
 
 def rtopk_set_row_local(enable):
     return load().rtopk_set_row_local(enable)
+
+
+def rtopk_set_split(enable):
+    return load().rtopk_set_split(enable)
 
 
 def rtopk_set_waves(waves):

@@ -266,6 +266,16 @@ int rtopk_check(void *workspace, void *stream);
 int rtopk_set_row_local(int enable);
 
 /*
+ * Process-wide switch for tests and experiments: with per-piece publication
+ * in a grid that runs in rounds (more pieces than the GPU holds at once), the
+ * per-batch selection is by default a second launch over the published
+ * pieces (one workgroup per batch element, after every piece is done); 0
+ * selects each batch element inside the step kernel instead, by the
+ * workgroup that completes it. The results are the same. Always RTOPK_OK.
+ */
+int rtopk_set_split(int enable);
+
+/*
  * Top-k sampling with the same hierarchical selection. The LightSeq inference
  * article reports sampling-decode speedups next to its beam-search ones (its
  * results passage). Every row r < R of logits [R][V] is selected as a batch

@@ -151,6 +151,11 @@ def test_row_local_switch(lib):
     assert st == 0 and p.row_local == (1 if p.pieces_per_group % p.chunks == 0 else 0)
 
 
+def test_split_switch(lib):
+    assert rtopk.rtopk_set_split(0) == 0
+    assert rtopk.rtopk_set_split(1) == 0
+
+
 def test_release_without_workspaces_is_harmless(lib):
     rtopk.rtopk_release()
 

@@ -190,6 +190,29 @@ def test_row_local_and_published_paths_agree():
         rtopk.rtopk_set_row_local(1)
 
 
+def test_split_and_in_kernel_selection_agree():
+    # per-piece publication in rounds (more pieces than the GPU holds at once):
+    # the per-batch selection runs as a second launch by default, inside the
+    # step kernel with the switch off; both must match the oracle and each other
+    cases = [synth.make_step("mixed250k"),
+             synth.make_custom(64, 8, 8, 60000, synth.BF16, seed=91, n_finished=9),
+             synth.make_custom(40, 6, 5, 70000, synth.F32, seed=92, n_finished=4)]
+    for s in cases:
+        st, p = rtopk.rtopk_plan(None, s.B, s.beam, s.V, s.k, s.dtype)
+        assert st == 0 and p.row_local == 0 and s.B * s.beam * p.chunks > 4096, s.name
+    for s in cases:
+        print(f"[parity split] {s.name}", flush=True)
+        got_split = run(s)
+        check(s, got_split, nthreads=16)
+        assert rtopk.rtopk_set_split(0) == 0
+        try:
+            got_in = run(s)
+        finally:
+            rtopk.rtopk_set_split(1)
+        for a, b in zip(got_split, got_in):
+            assert np.array_equal(a, b), s.name
+
+
 @pytest.mark.parametrize("nv", [1, 2, 3, 4, 6, 8, 10, 12])
 def test_every_tile_variant(nv):
     cases = [synth.make_custom(4, 4, 4, 40000, synth.F16, seed=300 + nv, sigma=3.0, n_finished=1),
